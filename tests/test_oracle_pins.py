@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle against what the pages and the mathematics fix, independent of the
+oracle's own code: closed forms, invariants, exhaustive search, exact rational arithmetic, library
+routines for the special cases, and a hand-derived worked case (tests/golden/tiny_layer_L3.json).
+"""
+
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def harmonic(n):
+    return sum(1.0 / m for m in range(1, n + 1))
+
+
+# -- worked case -----------------------------------------------------------------------------------
+
+def test_golden_tiny_layer():
+    g = json.load(open(os.path.join(GOLDEN, "tiny_layer_L3.json")))
+    i = g["inputs"]
+    col = lambda v: np.array(v, dtype=np.float64).reshape(i["L"], 1, 1)
+    out = oracle.layer(col(i["Q"]), col(i["K"]), col(i["V"]), col(i["X"]), i["tau"], i["q"])
+    ex = g["expected"]
+    np.testing.assert_allclose(out["s_h"][0], ex["s_h"], rtol=1e-14)
+    np.testing.assert_allclose(out["s_l"], ex["s_l"], rtol=1e-14)
+    assert (out["k"], out["Lp"]) == (ex["k"], ex["Lp"])
+    assert out["idx"][0].tolist() == ex["idx"]
+    np.testing.assert_allclose(out["Oh"][0, :, 0], ex["O_hat"], rtol=1e-14)
+    np.testing.assert_allclose(out["Y"][:, 0, 0], ex["Y"], rtol=1e-14)
+
+
+# -- scoring --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L,q", [(1, 1), (7, 3), (64, 16), (200, 16), (300, 64)])
+def test_score_zero_keys_closed_form(L, q):
+    """K = 0: every visible logit is 0, so query p spreads 1/(p+1) over keys 0..p and
+    s_h[t] = H_L - H_max(t, L-q) (harmonic numbers)."""
+    Hq, Hkv, d = 4, 2, 8
+    Q = rnd((L, Hq, d), 1)
+    s = oracle.head_scores(Q, np.zeros((L, Hkv, d)), q)
+    H = [harmonic(n) for n in range(L + 1)]
+    want = np.array([H[L] - H[max(t, L - q)] for t in range(L)])
+    for h in range(Hq):
+        np.testing.assert_allclose(s[h], want, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_score_rows_are_distributions(seed):
+    L, Hq, Hkv, d, q = 97, 6, 3, 16, 11
+    s = oracle.head_scores(rnd((L, Hq, d), seed, 2.0), rnd((L, Hkv, d), seed + 10, 2.0), q)
+    np.testing.assert_allclose(s.sum(axis=1), q, rtol=1e-13)
+    assert (s > 0).all()
+    # the last q-1 keys are invisible to the earlier recent queries: key L-1 only to the last one
+    assert (s[:, -1] <= 1.0 + 1e-15).all()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_score_matches_library_attention_weights(seed):
+    """With V = identity, scaled_dot_product_attention returns the attention weights themselves, so
+    its column sums over the recent queries are s_h; the library applies its own scale 1/sqrt(d)."""
+    L, Hq, Hkv, d, q = 40, 4, 2, 8, 5
+    Q, K = rnd((L, Hq, d), seed), rnd((L, Hkv, d), seed + 100)
+    s = oracle.head_scores(Q, K, q)
+    G = Hq // Hkv
+    recent = torch.arange(L - q, L)
+    mask = torch.arange(L)[None, :] <= recent[:, None]
+    for h in range(Hq):
+        qt = torch.from_numpy(Q[L - q:, h, :])[None, None]
+        kt = torch.from_numpy(K[:, h // G, :])[None, None]
+        w = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, torch.eye(L, dtype=torch.float64)[None, None], attn_mask=mask[None, None])
+        np.testing.assert_allclose(s[h], w[0, 0].sum(0).numpy(), rtol=1e-12)
+
+
+def test_layer_score_normalised_and_equal_heads():
+    L, d, q = 50, 8, 7
+    Q1 = rnd((L, 1, d), 3)
+    Q = np.repeat(Q1, 4, axis=1)
+    K = rnd((L, 1, d), 4)
+    s_h = oracle.head_scores(Q, K, q)
+    s_l = oracle.layer_score(s_h)
+    assert abs(s_l.sum() - 1) < 1e-14
+    np.testing.assert_allclose(s_l, s_h[0] / q, rtol=1e-12)
+
+
+# -- budget ---------------------------------------------------------------------------------------
+
+def brute_budget(vals, tau):
+    """k = min { j : min over j-subsets of the exact sum >= tau }, in exact rationals."""
+    fv = [Fraction(v) for v in vals]
+    ft = Fraction(tau)
+    for j in range(len(fv) + 1):
+        c = min(sum(c_, Fraction(0)) for c_ in itertools.combinations(fv, j)) if j else Fraction(0)
+        if c >= ft:
+            return j
+    return len(fv)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_budget_exhaustive_exact(seed):
+    """Dyadic values (multiples of 2^-20) keep every partial sum exact in fp64, so thresholds can sit
+    exactly on a partial sum and test >= against > (the notes' inequality)."""
+    r = np.random.default_rng(seed)
+    L = int(r.integers(1, 9))
+    v = r.integers(1, 2000, size=L).astype(np.float64)
+    if seed % 3 == 0:
+        v = np.round(v / 500) * 500 + 1          # ties
+    v = v * 2.0 ** -20
+    srt = np.sort(v)
+    taus = [0.0, 1e-9, float(srt[0]), float(srt[: max(1, L // 2)].sum()),
+            float(srt[: max(1, L // 2)].sum()) + 2.0 ** -21, float(v.sum()), float(v.sum()) * 2]
+    for tau in taus:
+        assert oracle.budget(v, tau)[0] == brute_budget(v, tau), (L, tau)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_budget_coverage_invariant_and_monotone(seed):
+    r = np.random.default_rng(seed)
+    L = 2000
+    v = r.gamma(0.5, size=L)
+    v /= v.sum()
+    srt = [Fraction(x) for x in np.sort(v)]
+    prev = 0
+    for tau in np.linspace(0, 0.98, 25):
+        k, Lp = oracle.budget(v, tau)
+        assert k + Lp == L and k >= prev
+        prev = k
+        ft = Fraction(float(tau))
+        assert sum(srt[:k], Fraction(0)) >= ft                     # covers tau
+        if k > 0:
+            assert sum(srt[: k - 1], Fraction(0)) < ft             # and is minimal
+    assert oracle.budget(v, 0.0) == (0, L)
+    assert oracle.budget(v, 2.0) == (L, 0)
+
+
+# -- selection ------------------------------------------------------------------------------------
+
+def brute_select(scores, Lp):
+    """Max-sum subset of size L'; among equal sums the lexicographically smallest index tuple."""
+    best = None
+    for c in itertools.combinations(range(len(scores)), Lp):
+        key = (-sum(scores[i] for i in c), c)
+        if best is None or key < best:
+            best = key
+    return list(best[1])
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_select_exhaustive_with_ties(seed):
+    r = np.random.default_rng(seed)
+    L = int(r.integers(2, 11))
+    s = r.integers(0, 4, size=(3, L)).astype(np.float64)        # many exact ties
+    for Lp in range(L + 1):
+        idx = oracle.select(s, Lp)
+        for h in range(3):
+            assert idx[h].tolist() == brute_select(s[h].tolist(), Lp)
+
+
+def test_select_nested_and_ascending():
+    s = rnd((5, 300), 7) ** 2
+    prev = [set() for _ in range(5)]
+    for Lp in range(0, 301, 17):
+        idx = oracle.select(s, Lp)
+        for h in range(5):
+            assert (np.diff(idx[h]) > 0).all()
+            assert prev[h] <= set(idx[h].tolist())
+            prev[h] = set(idx[h].tolist())
+
+
+def test_select_zero_keys_keeps_the_prefix():
+    """K = 0 makes tokens 0..L-q exactly tied at the top and later tokens strictly smaller, so the
+    lower-index tie-break keeps exactly the first L' tokens."""
+    L, q = 120, 16
+    s = oracle.head_scores(rnd((L, 2, 8), 1), np.zeros((L, 2, 8)), q)
+    for Lp in (1, 50, L - q + 1, L - 3, L):
+        idx = oracle.select(s, Lp)
+        assert (idx == np.arange(Lp)[None, :]).all()
+
+
+# -- attention ------------------------------------------------------------------------------------
+
+def sdpa_causal(q, k, v):
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=True)[0, 0].numpy()
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_dense_attention_matches_library(seed):
+    L, Hq, Hkv, d = 70, 4, 2, 16
+    Q, K, V = rnd((L, Hq, d), seed, 1.5), rnd((L, Hkv, d), seed + 1, 1.5), rnd((L, Hkv, d), seed + 2)
+    for h in range(Hq):
+        np.testing.assert_allclose(oracle.dense_attention_rows(Q, K, V, h),
+                                   sdpa_causal(Q[:, h], K[:, h // 2], V[:, h // 2]), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_compressed_attention_mask_by_position(seed):
+    """With ascending, unique positions, masking by original position equals the causal mask in the
+    compressed index (checked against the library's causal attention)."""
+    r = np.random.default_rng(seed)
+    n, d = 60, 8
+    pos = np.sort(r.choice(500, n, replace=False))
+    q, k, v = rnd((n, d), seed), rnd((n, d), seed + 1), rnd((n, d), seed + 2)
+    np.testing.assert_allclose(oracle.attention_rows(q, k, v, pos), sdpa_causal(q, k, v),
+                               rtol=1e-12, atol=1e-13)
+    # a row subset is the same rows of the full result
+    rows = [0, 5, 59]
+    np.testing.assert_allclose(oracle.attention_rows(q, k, v, pos, rows),
+                               oracle.attention_rows(q, k, v, pos)[rows], rtol=1e-14)
+
+
+def test_attention_closed_forms():
+    n, d = 50, 8
+    pos = np.arange(n) * 3
+    v = rnd((n, d), 2)
+    # zero keys: uniform weights over the visible prefix
+    out = oracle.attention_rows(rnd((n, d), 1), np.zeros((n, d)), v, pos)
+    want = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    np.testing.assert_allclose(out, want, rtol=1e-13)
+    # constant values: the output is that constant
+    c = np.tile(rnd((1, d), 5), (n, 1))
+    np.testing.assert_allclose(oracle.attention_rows(rnd((n, d), 3), rnd((n, d), 4), c, pos), c,
+                               rtol=1e-13)
+    # row 0 sees only itself: exactly V[0]
+    assert (oracle.attention_rows(rnd((n, d), 6), rnd((n, d), 7), v, pos)[0] == v[0]).all()
+
+
+# -- decompress / residual / whole layer ----------------------------------------------------------
+
+def test_decompress_compress_roundtrip_and_zero_rows():
+    L, Hq, d = 40, 3, 4
+    M = rnd((L, Hq, d), 1)
+    idx = oracle.select(rnd((Hq, L), 2) ** 2, 17)
+    Mh = np.stack([M[idx[h], h] for h in range(Hq)])
+    O = oracle.decompress(Mh, idx, L)
+    for h in range(Hq):
+        keep = np.zeros(L, bool)
+        keep[idx[h]] = True
+        assert (O[keep, h] == M[keep, h]).all()
+        assert (O[~keep, h] == 0).all() and not np.signbit(O[~keep, h]).any()
+    X = rnd((L, Hq, d), 3)
+    Y = oracle.residual(X, O)
+    for h in range(Hq):
+        un = np.setdiff1d(np.arange(L), idx[h])
+        assert (Y[un, h] == X[un, h]).all()
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_tau_zero_layer_is_dense_attention_plus_residual(seed):
+    L, Hq, Hkv, d, q = 64, 4, 2, 8, 8
+    Q, K, V, X = (rnd((L, Hq, d), seed), rnd((L, Hkv, d), seed + 1), rnd((L, Hkv, d), seed + 2),
+                  rnd((L, Hq, d), seed + 3))
+    out = oracle.layer(Q, K, V, X, 0.0, q)
+    assert out["Lp"] == L
+    np.testing.assert_allclose(out["Y"], oracle.dense_layer(Q, K, V, X), rtol=1e-13, atol=1e-13)
+    for h in range(Hq):
+        np.testing.assert_allclose(out["Y"][:, h] - X[:, h],
+                                   sdpa_causal(Q[:, h], K[:, h // 2], V[:, h // 2]), rtol=1e-11, atol=1e-12)
+
+
+def test_tau_near_one_drops_everything_but_coverage():
+    L, d = 30, 8
+    Q, K, V, X = rnd((L, 2, d), 1), rnd((L, 2, d), 2), rnd((L, 2, d), 3), rnd((L, 2, d), 4)
+    out = oracle.layer(Q, K, V, X, 1.5, 4)
+    assert out["Lp"] == 0 and (out["Y"] == X).all()
+
+
+# -- storage rounding and load-time layer choice --------------------------------------------------
+
+def test_round_to_storage_matches_library_conversion():
+    r = np.random.default_rng(0)
+    a = torch.from_numpy(r.standard_normal(20000).astype(np.float32)).to(torch.bfloat16)
+    b = torch.from_numpy(r.standard_normal(20000).astype(np.float32) * 1e-3).to(torch.bfloat16)
+    exact = a.double().numpy() + b.double().numpy()
+    want = (a.float() + b.float()).to(torch.bfloat16).double().numpy()
+    assert (oracle.round_to_storage(exact, "bf16") == want).all()
+    x = r.standard_normal(1000) * 7
+    assert (oracle.round_to_storage(x, "f32") == x.astype(np.float32).astype(np.float64)).all()
+    halfway = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8])     # ties go to even
+    assert oracle.round_to_storage(halfway, "bf16").tolist() == [1.0, 1.0 + 4 * 2.0 ** -8]
+
+
+def test_sparse_layers_and_drift():
+    R = [0.4, 0.3, 0.5, 0.1, 0.2, 0.05, 0.45, 0.35]
+    assert oracle.sparse_layers(R) == [2, 4, 5, 6]
+    assert oracle.sparse_layers([0.2] * 4) == [1, 2]                 # ties by layer id
+    assert oracle.sparse_layers(sorted(R, reverse=True)) == [5, 6, 7, 8]
+    h = rnd((100, 16), 1)
+    assert abs(oracle.representation_drift(h, h * 1.25, eps=0.0) - 0.25) < 1e-14
+    assert oracle.representation_drift(h, h) == 0.0
+
+
+# -- planted mistakes must trip a pin ---------------------------------------------------------------
+
+def _mut_no_causal(Q, K, q):
+    L, Hq, d = Q.shape
+    s = np.zeros((Hq, L))
+    for h in range(Hq):
+        z = Q[L - q:, h] @ K[:, h * K.shape[1] // Hq].T / np.sqrt(d)
+        e = np.exp(z - z.max(1, keepdims=True))
+        s[h] = (e / e.sum(1, keepdims=True)).sum(0)
+    return s
+
+
+def _mut_budget_strict(s_l, tau):
+    C = np.concatenate([[0.0], np.cumsum(np.sort(s_l))])
+    hit = np.nonzero(C > tau)[0]
+    k = int(hit[0]) if len(hit) else len(s_l)
+    return k, len(s_l) - k
+
+
+def _mut_select_high_index_ties(s_h, Lp):
+    L = s_h.shape[1]
+    return np.stack([np.sort(np.lexsort((-np.arange(L), -s_h[h]))[:Lp]) for h in range(s_h.shape[0])])
+
+
+def _mut_attention_no_scale(Qh, Kh, Vh, pos, rows=None):
+    n, d = Qh.shape
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    z = Qh[rows] @ Kh.T
+    z = np.where(pos[None, :] <= pos[rows][:, None], z, -np.inf)
+    e = np.exp(z - z.max(1, keepdims=True))
+    return e / e.sum(1, keepdims=True) @ Vh
+
+
+@pytest.mark.parametrize("name,mutant,pin", [
+    ("head_scores", _mut_no_causal, lambda: test_score_zero_keys_closed_form(64, 16)),
+    ("budget", _mut_budget_strict, lambda: test_budget_exhaustive_exact(0)),
+    ("select", _mut_select_high_index_ties, test_select_zero_keys_keeps_the_prefix),
+    ("attention_rows", _mut_attention_no_scale, lambda: test_dense_attention_matches_library(0)),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, mutant, pin):
+    monkeypatch.setattr(oracle, name, mutant)
+    monkeypatch.setattr(oracle.tsa_oracle, name, mutant)
+    with pytest.raises(AssertionError):
+        pin()
