@@ -1,0 +1,223 @@
+"""Benchmark of the Token Sparse Attention prefill layer on one MI355X.
+
+One step = one full layer (score -> budget -> select -> gather -> compressed causal attention ->
+scatter + residual) through the C ABI on the L = 131072, 32/8-head, d = 128, bf16 workload with
+inputs resident in HBM.  Prints one JSON line: the layer latency, the speedup over this library's
+own dense causal attention on the full length, per-stage times with their roofline fractions, the
+roofline of the dominant kernel (the compressed attention, bf16 matrix cores) and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from token_sparse_attention_amd import binding  # noqa: E402
+from token_sparse_attention_amd.configs import CONFIGS  # noqa: E402
+from token_sparse_attention_amd.inputs import make_layer  # noqa: E402
+
+METRIC = "TSA layer ms & speedup vs own dense attn at L=128K; MFMA util, HBM GB/s"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+
+
+def timed(fn, steps, warmup, stream):
+    """Mean ms per call of fn() over `steps` calls, HIP events on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps
+
+
+def algorithmic(cfg, Lp, union_rows):
+    """Bytes (or flops) each stage must move (or compute) by definition, independent of how."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    L, Hq, Hkv, d, q = cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.q
+    return {
+        "score": L * Hkv * d * e + q * Hq * d * e + 4 * Hq * L + 4 * L,
+        "budget": 4 * L + 8,
+        "select": 4 * Hq * L + 4 * Hq * Lp + 4 * Hq * L,
+        "gather": Hq * Lp * d * e + 2 * union_rows * d * e + 4 * Hq * Lp + 3 * Hq * Lp * d * e,
+        "scatter": 2 * L * Hq * d * e + Hq * Lp * d * e + 4 * Hq * L,
+        "attn_flops": 4 * d * Hq * Lp * (Lp + 1) // 2,
+        "dense_flops": 4 * d * Hq * L * (L + 1) // 2,
+    }
+
+
+def cpu_baseline(cfg, inp, Lp_gpu, budget_s=20.0):
+    """The CPU oracle (float64, as it stands) on a bounded sample of the same workload, scaled to
+    one full layer: scoring, budget and selection run in full; gather + attention run on a sample of
+    output rows of a few heads and are scaled by the exact causal pair count; decompress + residual
+    runs on a sample of rows and is scaled by the row count."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    f64 = lambda t: t.double().numpy()
+    Q, K, V, X = (f64(inp[n]) for n in ("Q", "K", "V", "X"))
+    t0 = time.perf_counter()
+    s_h = oracle.head_scores(Q, K, cfg.q)
+    s_l = oracle.layer_score(s_h)
+    k, Lp = oracle.budget(s_l, float(np.float32(cfg.tau)))
+    idx = oracle.select(s_h, Lp)
+    t_sel = time.perf_counter() - t0
+    # attention on sampled rows of sampled heads; pair count of row i is i + 1
+    rng = np.random.default_rng(0)
+    heads = [0, cfg.Hq // 2]
+    rows = np.sort(rng.choice(Lp, 24, replace=False))
+    t0 = time.perf_counter()
+    for h in heads:
+        g = oracle.gqa_group(h, cfg.Hq, cfg.Hkv)
+        qh, kh, vh = Q[idx[h], h, :], K[idx[h], g, :], V[idx[h], g, :]
+        oracle.attention_rows(qh, kh, vh, idx[h], rows)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t_att = time.perf_counter() - t0
+    sampled_pairs = len(heads) * float(np.sum(rows + 1))
+    total_pairs = cfg.Hq * Lp * (Lp + 1) / 2.0
+    t_att_full = t_att * total_pairs / sampled_pairs
+    # decompress + residual on a sample of rows (cost linear in rows)
+    n_rows = 4096
+    t0 = time.perf_counter()
+    Oh = np.zeros((cfg.Hq, n_rows, cfg.d))
+    oracle.residual(X[:n_rows], oracle.decompress(Oh, np.tile(np.arange(n_rows), (cfg.Hq, 1)), n_rows))
+    t_sc = (time.perf_counter() - t0) * cfg.L / n_rows
+    total_ms = 1e3 * (t_sel + t_att_full + t_sc)
+    return {"value": round(total_ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": (f"numpy float64 oracle on this workload: scoring, budget and selection in full "
+                       f"({t_sel:.1f} s); gather+attention on {len(rows)} rows x {len(heads)} heads "
+                       f"({t_att:.1f} s) scaled by causal pair count to {cfg.Hq} heads x L'={Lp}; "
+                       f"decompress+residual on {n_rows} rows scaled to L={cfg.L}"),
+            "oracle_k": int(k), "oracle_Lp": int(Lp), "gpu_Lp": int(Lp_gpu)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", type=int, default=4, help="workload number (4 = L=128K headline)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the layer runs on one MI355X (no multi-GPU path is built); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    binding.lib()
+    t_gen = time.perf_counter()
+    inp = make_layer(cfg)
+    t_gen = time.perf_counter() - t_gen
+    Q, K, V, X = (inp[n].to(dev) for n in ("Q", "K", "V", "X"))
+    s = binding.shape_of(cfg)
+    C = binding.capacity(cfg.L)
+    stream = torch.cuda.current_stream()
+
+    # -- the whole layer --------------------------------------------------------------------------
+    ws = binding.workspace(binding.layer_workspace_bytes(s), dev)
+    kLp = torch.zeros(2, dtype=torch.int32, device=dev)
+    Y = torch.empty_like(X)
+    layer_ms = timed(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws), args.steps, args.warmup, stream)
+    k, Lp = kLp.tolist()
+
+    # -- the dense baseline -----------------------------------------------------------------------
+    dws = binding.workspace(binding.dense_workspace_bytes(s), dev)
+    Yd = torch.empty_like(X)
+    dense_ms = timed(lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws), args.steps, args.warmup, stream)
+    del dws, Yd
+
+    # -- stage by stage (same kernels, separate buffers) --------------------------------------------
+    sws = binding.workspace(binding.stage_workspace_bytes(s), dev)
+    s_h = torch.empty(cfg.Hq, cfg.L, dtype=torch.float32, device=dev)
+    s_l = torch.empty(cfg.L, dtype=torch.float32, device=dev)
+    kl = torch.zeros(2, dtype=torch.int32, device=dev)
+    idx = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
+    inv = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
+    Qh = torch.empty(cfg.Hq, C, cfg.d, dtype=Q.dtype, device=dev)
+    Kh = torch.empty_like(Qh)
+    Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
+    Oh = torch.empty_like(Qh)
+    Ys = torch.empty_like(X)
+    st = {}
+    st["score"] = timed(lambda: binding.score(s, Q, K, s_h, s_l, sws), args.steps, 1, stream)
+    st["budget"] = timed(lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws), args.steps, 1, stream)
+    st["select"] = timed(lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws), args.steps, 1, stream)
+    st["gather"] = timed(lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht), args.steps, 1, stream)
+    st["attention"] = timed(lambda: binding.attn_causal(s, Qh, Kh, Vht, kl[1:2], Oh), args.steps, 1, stream)
+    st["scatter"] = timed(lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Ys), args.steps, 1, stream)
+    assert kl.tolist() == [k, Lp]
+    # rows of K/V actually read by the gather: the union of the selections of each KV group
+    G = cfg.Hq // cfg.Hkv
+    sel = idx[:, :Lp].cpu().numpy()
+    union_rows = sum(len(np.unique(sel[g * G:(g + 1) * G])) for g in range(cfg.Hkv))
+    alg = algorithmic(cfg, Lp, union_rows)
+
+    def gbs(nbytes, ms):
+        return nbytes / (ms * 1e-3) / 1e9
+
+    stages = {}
+    for name in ("score", "budget", "select", "gather", "scatter"):
+        rate = gbs(alg[name], st[name])
+        stages[name] = {"ms": round(st[name], 4), "algorithmic_bytes": int(alg[name]), "GB_s": round(rate, 1),
+                        "hbm_frac": round(rate / HBM_PEAK_GBS, 4)}
+    att_tf = alg["attn_flops"] / (st["attention"] * 1e-3) / 1e12
+    stages["attention"] = {"ms": round(st["attention"], 4), "algorithmic_flops": int(alg["attn_flops"]),
+                           "TFLOP_s": round(att_tf, 1), "mfma_frac": round(att_tf / BF16_PEAK_TFLOPS, 4)}
+    dense_tf = alg["dense_flops"] / (dense_ms * 1e-3) / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": round(layer_ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(layer_ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d, "q": cfg.q,
+                   "tau": cfg.tau, "seed": cfg.seed, "k": k, "L_keep": Lp, "parallelism": "single GPU"},
+        "dense_ms": round(dense_ms, 3),
+        "speedup_vs_dense": round(dense_ms / layer_ms, 4),
+        "attention_only_speedup": round(dense_ms / st["attention"], 4),
+        "dense_TFLOP_s": round(dense_tf, 1),
+        "dense_mfma_frac": round(dense_tf / BF16_PEAK_TFLOPS, 4),
+        "overhead_frac_of_attention": round((layer_ms - st["attention"]) / st["attention"], 4),
+        "stages": stages,
+        "roofline": {"bound": "mfma", "kernel": "compressed causal attention (bf16)", "achieved": round(att_tf, 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, Lp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,123 @@
+"""Host-side checks of the C ABI: the library loads, exports every function include/tsa.h declares,
+and rejects bad arguments before launching anything (so these run without a GPU)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from token_sparse_attention_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tsa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(tsa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_binding_surface():
+    assert set(declared_functions()) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def good():
+    return binding.shape(4096, 32, 8, 128, 16, 0.005, "bf16")
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("dtype", 7, 3), ("tau", -0.1, 1), ("tau", 1.0, 1), ("tau", math.nan, 1),
+    ("L", 0, 2), ("L", 1 << 31, 2), ("Hq", 0, 2), ("Hkv", 3, 2), ("Hkv", 64, 2), ("q", 0, 2),
+    ("q", 4097, 2), ("q", 2000, 2), ("d", 96, 7), ("d", 256, 7),
+])
+def test_check_args_rejects(field, value, status):
+    s = good()
+    setattr(s, field, value)
+    assert binding.check_args(s) == status
+
+
+def test_check_args_accepts_the_workloads():
+    from token_sparse_attention_amd.configs import CONFIGS
+    for cfg in CONFIGS.values():
+        assert binding.check_args(binding.shape_of(cfg)) == 0
+    s = good()
+    s.q = s.L = 7
+    assert binding.check_args(s) == 0
+
+
+def test_status_strings():
+    L = binding.lib()
+    for code in range(8):
+        assert L.tsa_status_string(code).decode() == binding._STATUS[code]
+    assert L.tsa_status_string(99).decode() == "unknown status"
+
+
+def test_capacity_and_workspace_sizes():
+    assert [binding.capacity(n) for n in (1, 256, 257, 1000)] == [256, 256, 512, 1024]
+    small, big = good(), good()
+    big.L = 131072
+    for fn in (binding.stage_workspace_bytes, binding.layer_workspace_bytes, binding.dense_workspace_bytes):
+        assert 0 < fn(small) < fn(big)
+        assert fn(small) % 256 == 0
+    bad = good()
+    bad.d = 96
+    assert binding.layer_workspace_bytes(bad) == 0
+    # the layer workspace holds Q_hat, K_hat, V_hat and O_hat at capacity
+    s = good()
+    assert binding.layer_workspace_bytes(s) >= 4 * 32 * binding.capacity(4096) * 128 * 2
+
+
+class FakePtr:
+    """Stands in for a tensor: only its address is used, and nothing is launched on these paths."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def test_entry_points_validate_before_launch():
+    s = good()
+    p = FakePtr(1 << 20)           # aligned, never dereferenced: every call below fails validation
+    mis = FakePtr((1 << 20) + 2)
+    with pytest.raises(binding.TsaError) as e:
+        binding.score(s, None, p, p, ws=None, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(binding.TsaError) as e:
+        binding.score(s, mis, p, p, stream=0)
+    assert e.value.status == 4
+    with pytest.raises(binding.TsaError) as e:           # missing workspace
+        binding.score(s, p, p, p, stream=0)
+    assert e.value.status == 5
+    with pytest.raises(binding.TsaError) as e:
+        binding.layer(s, p, p, p, None, None, stream=0)
+    assert e.value.status == 1
+    bad = good()
+    bad.tau = 2.0
+    with pytest.raises(binding.TsaError) as e:
+        binding.attn_causal(bad, p, p, p, p, p, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(binding.TsaError) as e:
+        binding.select(s, p, None, p, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(binding.TsaError) as e:
+        binding.scatter_residual(s, p, None, None, p, None, p, stream=0)    # no inv and no idx
+    assert e.value.status == 1
+
+
+def test_select_sparse_layers_rule():
+    from token_sparse_attention_amd.configs import CONFIGS
+    from token_sparse_attention_amd.inputs import chain_drift_values
+    from token_sparse_attention_amd.runtime import select_sparse_layers
+    cfg = CONFIGS[5]
+    assert select_sparse_layers(chain_drift_values(cfg)) == list(cfg.sparse_layers)
+    assert select_sparse_layers([0.3, 0.1, 0.2, 0.1]) == [2, 4]

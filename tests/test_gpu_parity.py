@@ -1,0 +1,347 @@
+"""HIP path vs the CPU oracle, stage by stage and end to end, through the C ABI.
+
+Acceptance rules (restated from the method's parity bar):
+  score      : s_h, s_l within 2e-7 relative (the HIP scores are float64 sums stored as float32)
+  budget     : k exact on the HIP's own float32 s_l (exact rational check), and against the oracle
+               either equal or inside the band C(k) >= tau(1-1e-5), C(k-1) < tau(1+1e-5)
+  select     : exact top-L' (score desc, index asc) of the HIP's own s_h; against the oracle only
+               ties within 1e-6 relative of the boundary score may differ
+  gather     : bit-exact;  scatter/decompress: bit-exact, zero rows +0.0
+  attention  : |gpu - oracle| <= 2e-2 + 1e-2 |oracle| (bf16), 1e-4 + 1e-4 |oracle| (f32), run on
+               the oracle's index sets; row 0 of every head is exactly V_hat[0]
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_sparse_attention_amd import binding
+from token_sparse_attention_amd.configs import CONFIGS, Workload, scaled
+from token_sparse_attention_amd.inputs import make_layer
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
+
+SMALL = {
+    "c1": CONFIGS[1],
+    "c2": CONFIGS[2],
+    "gqa_ragged_q5": Workload("gqa_ragged_q5", L=1000, Hq=4, Hkv=2, d=128, q=5, tau=0.05, dtype="bf16",
+                              salient_frac=0.02, shared_frac=0.5, seed=11),
+    "d64_bf16_odd": Workload("d64_bf16_odd", L=777, Hq=2, Hkv=1, d=64, q=16, tau=0.01, dtype="bf16",
+                             salient_frac=0.03, shared_frac=0.5, sink=8, seed=12),
+    "f32_d128": Workload("f32_d128", L=300, Hq=2, Hkv=2, d=128, q=3, tau=0.02, dtype="f32",
+                         salient_frac=0.05, shared_frac=1.0, seed=13),
+    "tiny_L1": Workload("tiny_L1", L=1, Hq=2, Hkv=1, d=64, q=1, tau=0.0, dtype="bf16",
+                        salient_frac=0.0, shared_frac=1.0, seed=14),
+    "tiny_L37": Workload("tiny_L37", L=37, Hq=8, Hkv=2, d=128, q=7, tau=0.1, dtype="bf16",
+                         salient_frac=0.1, shared_frac=0.5, seed=15),
+}
+
+
+def f64(t):
+    return t.double().cpu().numpy()
+
+
+def tau32(cfg):
+    return float(np.float32(cfg.tau))
+
+
+class Case:
+    """Inputs on host and device plus the oracle's stage outputs (computed lazily)."""
+
+    def __init__(self, cfg, dev):
+        self.cfg, self.dev = cfg, dev
+        self.inp = make_layer(cfg)
+        self.d = {n: self.inp[n].to(dev) for n in ("Q", "K", "V", "X")}
+        self.h = {n: f64(self.inp[n]) for n in ("Q", "K", "V", "X")}
+        self.s = binding.shape_of(cfg)
+        self.C = binding.capacity(cfg.L)
+        self._ref = None
+
+    @property
+    def ref(self):
+        if self._ref is None:
+            r = {"s_h": oracle.head_scores(self.h["Q"], self.h["K"], self.cfg.q)}
+            r["s_l"] = oracle.layer_score(r["s_h"])
+            r["k"], r["Lp"] = oracle.budget(r["s_l"], tau32(self.cfg))
+            r["idx"] = oracle.select(r["s_h"], r["Lp"])
+            self._ref = r
+        return self._ref
+
+    def empty(self, *shape, dtype=None):
+        return torch.empty(*shape, dtype=dtype or self.d["Q"].dtype, device=self.dev)
+
+    def idx_tensor(self, idx):
+        """[Hq][L] int32 whose first L' columns hold idx (the rest -1) and the matching inverse map."""
+        Hq, L = self.cfg.Hq, self.cfg.L
+        full = np.full((Hq, L), -1, dtype=np.int32)
+        inv = np.full((Hq, L), -1, dtype=np.int32)
+        full[:, : idx.shape[1]] = idx
+        for h in range(Hq):
+            inv[h, idx[h]] = np.arange(idx.shape[1])
+        return torch.from_numpy(full).to(self.dev), torch.from_numpy(inv).to(self.dev)
+
+    def lp_tensor(self, Lp):
+        return torch.tensor([Lp], dtype=torch.int32, device=self.dev)
+
+    def stage_ws(self):
+        return binding.workspace(binding.stage_workspace_bytes(self.s), self.dev)
+
+    def gpu_scores(self):
+        s_h = torch.empty(self.cfg.Hq, self.cfg.L, dtype=torch.float32, device=self.dev)
+        s_l = torch.empty(self.cfg.L, dtype=torch.float32, device=self.dev)
+        binding.score(self.s, self.d["Q"], self.d["K"], s_h, s_l, self.stage_ws())
+        return s_h, s_l
+
+    def gpu_budget(self, s_l):
+        kl = torch.zeros(2, dtype=torch.int32, device=self.dev)
+        binding.budget(self.s, s_l, kl[0:1], kl[1:2], self.stage_ws())
+        return [int(v) for v in kl.tolist()]
+
+    def gpu_select(self, s_h, Lp):
+        idx = torch.full((self.cfg.Hq, self.cfg.L), -7, dtype=torch.int32, device=self.dev)
+        inv = torch.full((self.cfg.Hq, self.cfg.L), -7, dtype=torch.int32, device=self.dev)
+        binding.select(self.s, s_h, self.lp_tensor(Lp), idx, inv, self.stage_ws())
+        return idx.cpu().numpy(), inv.cpu().numpy()
+
+    def gpu_gather(self, idx):
+        Hq, d, C = self.cfg.Hq, self.cfg.d, self.C
+        it, _ = self.idx_tensor(idx)
+        Qh, Kh, Vht = self.empty(Hq, C, d), self.empty(Hq, C, d), self.empty(Hq, d, C)
+        binding.gather(self.s, self.d["Q"], self.d["K"], self.d["V"], it, self.lp_tensor(idx.shape[1]), Qh, Kh, Vht)
+        return Qh, Kh, Vht
+
+
+@pytest.fixture(scope="module", params=list(SMALL))
+def case(request, gpu):
+    torch.manual_seed(0)
+    return Case(SMALL[request.param], gpu)
+
+
+def assert_close(got, want, dtype, what):
+    atol, rtol = TOL[dtype]
+    bad = np.abs(got - want) > atol + rtol * np.abs(want)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside {atol}+{rtol}|ref|, "
+                           f"max |diff| {np.abs(got - want).max():.3e}")
+
+
+# -- stage 1 --------------------------------------------------------------------------------------
+
+def test_score(case):
+    s_h, s_l = case.gpu_scores()
+    r = case.ref
+    np.testing.assert_allclose(f64(s_h), r["s_h"], rtol=2e-7, atol=1e-30)
+    np.testing.assert_allclose(f64(s_l), r["s_l"], rtol=2e-7, atol=1e-30)
+
+
+# -- stage 2 --------------------------------------------------------------------------------------
+
+def exact_budget(vals32, tau):
+    """min k with (sum of the k smallest float32 values) >= tau, in exact integer arithmetic: every
+    float32 (and tau, a float32) times 2^149 is an integer."""
+    v = sorted(int(x * 2.0 ** 149) for x in vals32.astype(np.float64))
+    target = int(np.float64(tau) * 2.0 ** 149)
+    if target <= 0:
+        return 0
+    acc = 0
+    for j, iv in enumerate(v):
+        acc += iv
+        if acc >= target:
+            return j + 1
+    return len(v)
+
+
+def test_budget(case):
+    s_h, s_l = case.gpu_scores()
+    k, Lp = case.gpu_budget(s_l)
+    assert k + Lp == case.cfg.L
+    assert k == exact_budget(s_l.cpu().numpy(), tau32(case.cfg))
+    r = case.ref
+    if k != r["k"]:
+        C = np.concatenate([[0.0], np.cumsum(np.sort(r["s_l"]))])
+        t = tau32(case.cfg)
+        assert C[k] >= t * (1 - 1e-5) and (k == 0 or C[k - 1] < t * (1 + 1e-5)), (k, r["k"])
+
+
+# -- stage 3 --------------------------------------------------------------------------------------
+
+def check_selection(idx, inv, Lp, s_h_exact):
+    """idx[:, :L'] must be exactly the oracle's selection on these scores, inv its inverse."""
+    want = oracle.select(s_h_exact, Lp)
+    Hq, L = s_h_exact.shape
+    assert (idx[:, :Lp] == want).all()
+    for h in range(Hq):
+        w = np.full(L, -1)
+        w[want[h]] = np.arange(Lp)
+        assert (inv[h] == w).all()
+
+
+def test_select_exact_on_own_scores(case):
+    s_h, s_l = case.gpu_scores()
+    k, Lp = case.gpu_budget(s_l)
+    idx, inv = case.gpu_select(s_h, Lp)
+    check_selection(idx, inv, Lp, f64(s_h))
+
+
+def test_select_against_oracle_tie_band(case):
+    s_h, s_l = case.gpu_scores()
+    _, Lp = case.gpu_budget(s_l)
+    idx, _ = case.gpu_select(s_h, Lp)
+    r = case.ref
+    want = oracle.select(r["s_h"], Lp)
+    for h in range(case.cfg.Hq):
+        diff = np.setxor1d(idx[h, :Lp], want[h])
+        if len(diff):
+            b = np.sort(r["s_h"][h])[::-1][Lp - 1]
+            assert (np.abs(r["s_h"][h][diff] - b) <= 1e-6 * b).all(), (h, diff)
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.37, 1.0])
+def test_select_any_budget(case, frac):
+    """The selection stage on its own at other keep counts, including L' = 0 and L' = L."""
+    s_h, _ = case.gpu_scores()
+    Lp = int(round(frac * case.cfg.L))
+    idx, inv = case.gpu_select(s_h, Lp)
+    check_selection(idx, inv, Lp, f64(s_h))
+
+
+def test_select_with_planted_ties(gpu):
+    """Exactly tied scores across the boundary: the lower indices must win."""
+    cfg = SMALL["tiny_L37"]
+    c = Case(cfg, gpu)
+    rng = np.random.default_rng(5)
+    s = rng.integers(0, 5, size=(cfg.Hq, cfg.L)).astype(np.float32) * np.float32(0.125)
+    s_h = torch.from_numpy(s).to(gpu)
+    for Lp in (0, 1, 5, 18, 36, 37):
+        idx, inv = c.gpu_select(s_h, Lp)
+        check_selection(idx, inv, Lp, s.astype(np.float64))
+
+
+# -- stage 4: gather and attention ----------------------------------------------------------------
+
+def test_gather_bit_exact(case):
+    r = case.ref
+    idx, Lp = r["idx"], r["Lp"]
+    Qh, Kh, Vht = case.gpu_gather(idx)
+    oq, ok, ov = oracle.gather(case.h["Q"], case.h["K"], case.h["V"], idx)
+    assert (f64(Qh[:, :Lp]) == oq).all()
+    assert (f64(Kh[:, :Lp]) == ok).all()
+    assert (f64(Vht[:, :, :Lp]).transpose(0, 2, 1) == ov).all()
+
+
+def test_attention_on_oracle_sets(case):
+    r = case.ref
+    idx, Lp = r["idx"], r["Lp"]
+    Qh, Kh, Vht = case.gpu_gather(idx)
+    Oh = case.empty(case.cfg.Hq, case.C, case.cfg.d)
+    binding.attn_causal(case.s, Qh, Kh, Vht, case.lp_tensor(Lp), Oh)
+    got = f64(Oh[:, :Lp])
+    oq, ok, ov = oracle.gather(case.h["Q"], case.h["K"], case.h["V"], idx)
+    want = oracle.compressed_attention(oq, ok, ov, idx)
+    assert_close(got, want, case.cfg.dtype, "O_hat")
+    if Lp:
+        assert (got[:, 0] == ov[:, 0]).all()          # one visible key: weight exactly 1
+
+
+# -- stage 5 --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["inv", "idx"])
+def test_scatter_residual_bit_exact(case, mode):
+    cfg, r = case.cfg, case.ref
+    idx, Lp = r["idx"], r["Lp"]
+    it, iv = case.idx_tensor(idx)
+    g = torch.Generator().manual_seed(3)
+    Oh = torch.randn(cfg.Hq, case.C, cfg.d, generator=g).to(case.d["Q"].dtype).to(case.dev)
+    Oh_h = f64(Oh)[:, :Lp]
+    inv = iv if mode == "inv" else None
+    # out of place with residual
+    Y = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.scatter_residual(case.s, Oh, it, inv, case.lp_tensor(Lp), case.d["X"], Y)
+    want = oracle.round_to_storage(oracle.residual(case.h["X"], oracle.decompress(Oh_h, idx, cfg.L)), cfg.dtype)
+    assert (f64(Y) == want).all()
+    # pure decompress: selected rows copied bit for bit, the rest +0.0
+    Y0 = case.empty(cfg.L, cfg.Hq, cfg.d).fill_(7.0)
+    binding.scatter_residual(case.s, Oh, it, inv, case.lp_tensor(Lp), None, Y0)
+    dec = oracle.decompress(Oh_h, idx, cfg.L)
+    got0 = f64(Y0)
+    assert (got0 == dec).all() and not np.signbit(got0[dec == 0]).any()
+    # in place: Y aliases X
+    Xc = case.d["X"].clone()
+    binding.scatter_residual(case.s, Oh, it, inv, case.lp_tensor(Lp), Xc, Xc)
+    assert (f64(Xc) == want).all()
+
+
+# -- the whole layer ------------------------------------------------------------------------------
+
+def test_layer_end_to_end(case):
+    cfg = case.cfg
+    ws = binding.workspace(binding.layer_workspace_bytes(case.s), case.dev)
+    kl = torch.zeros(2, dtype=torch.int32, device=case.dev)
+    Y = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.layer(case.s, case.d["Q"], case.d["K"], case.d["V"], case.d["X"], Y, kl, ws)
+    k, Lp = kl.tolist()
+    # the same sets as the stage-by-stage calls (same kernels), checked against the oracle above
+    s_h, s_l = case.gpu_scores()
+    assert [k, Lp] == case.gpu_budget(s_l)
+    idx, _ = case.gpu_select(s_h, Lp)
+    idx = idx[:, :Lp].astype(np.int64)
+    oq, ok, ov = oracle.gather(case.h["Q"], case.h["K"], case.h["V"], idx)
+    Oh = oracle.compressed_attention(oq, ok, ov, idx)
+    want = oracle.residual(case.h["X"], oracle.decompress(Oh, idx, cfg.L))
+    assert_close(f64(Y), want, cfg.dtype, "Y")
+    # rows outside S_h carry X bit for bit
+    got = f64(Y)
+    for h in range(cfg.Hq):
+        un = np.setdiff1d(np.arange(cfg.L), idx[h])
+        assert (got[un, h] == case.h["X"][un, h]).all()
+    # deterministic: a second run is bitwise identical
+    Y2 = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.layer(case.s, case.d["Q"], case.d["K"], case.d["V"], case.d["X"], Y2, kl, ws)
+    assert torch.equal(Y, Y2) and kl.tolist() == [k, Lp]
+    # in place (Y aliases X) gives the same result
+    Xc = case.d["X"].clone()
+    binding.layer(case.s, case.d["Q"], case.d["K"], case.d["V"], Xc, Xc, None, ws)
+    assert torch.equal(Xc, Y)
+
+
+def test_dense_attention(case):
+    cfg = case.cfg
+    ws = binding.workspace(binding.dense_workspace_bytes(case.s), case.dev)
+    Y = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.dense_attn_causal(case.s, case.d["Q"], case.d["K"], case.d["V"], case.d["X"], Y, ws)
+    want = oracle.dense_layer(case.h["Q"], case.h["K"], case.h["V"], case.h["X"])
+    assert_close(f64(Y), want, cfg.dtype, "dense Y")
+    O = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.dense_attn_causal(case.s, case.d["Q"], case.d["K"], case.d["V"], None, O, ws)
+    assert_close(f64(O), want - case.h["X"], cfg.dtype, "dense O")
+
+
+def test_tau_zero_layer_equals_dense_plus_residual(gpu):
+    cfg = scaled(CONFIGS[2], 1536, Hq=4, Hkv=2, tau=0.0)
+    c = Case(cfg, gpu)
+    ws = binding.workspace(binding.layer_workspace_bytes(c.s), gpu)
+    kl = torch.zeros(2, dtype=torch.int32, device=gpu)
+    Y = c.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.layer(c.s, c.d["Q"], c.d["K"], c.d["V"], c.d["X"], Y, kl, ws)
+    assert kl.tolist() == [0, cfg.L]
+    want = oracle.dense_layer(c.h["Q"], c.h["K"], c.h["V"], c.h["X"])
+    assert_close(f64(Y), want, cfg.dtype, "tau=0 layer vs dense")
+
+
+def test_empty_keep_set_leaves_residual(gpu):
+    """L' = 0 through gather, attention and scatter: Y == X exactly, pure decompress all +0.0."""
+    cfg = SMALL["gqa_ragged_q5"]
+    c = Case(cfg, gpu)
+    idx = np.zeros((cfg.Hq, 0), dtype=np.int64)
+    Qh, Kh, Vht = c.gpu_gather(idx)
+    Oh = c.empty(cfg.Hq, c.C, cfg.d).fill_(3.0)
+    binding.attn_causal(c.s, Qh, Kh, Vht, c.lp_tensor(0), Oh)
+    assert (Oh == 3.0).all()                              # nothing written
+    it, iv = c.idx_tensor(idx)
+    Y = c.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.scatter_residual(c.s, Oh, it, iv, c.lp_tensor(0), c.d["X"], Y)
+    assert torch.equal(Y, c.d["X"])
+    binding.scatter_residual(c.s, Oh, it, iv, c.lp_tensor(0), None, Y)
+    assert (Y == 0).all() and not torch.signbit(Y).any()

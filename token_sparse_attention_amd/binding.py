@@ -1,0 +1,176 @@
+"""ctypes binding of libtsa.so.  Argument marshalling only: every step runs in the library's HIP
+kernels.  torch tensors supply device memory (``data_ptr()``) and the stream
+(``torch.cuda.current_stream()``); nothing here computes.  A missing library is an error."""
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsa.so")
+_lib = None
+
+F32, BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "unsupported dtype",
+           4: "tensor not 16-byte aligned", 5: "workspace missing, misaligned or too small",
+           6: "HIP launch failed", 7: "not implemented for these parameters"}
+
+
+class TsaError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed with status {status} ({_STATUS.get(status, 'unknown')})")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int64), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("q", ctypes.c_int32), ("tau", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+# name -> argument types after the leading `const tsa_shape*`
+_P = ctypes.c_void_p
+_SIGS = {
+    "tsa_score": [_P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_budget": [_P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_select": [_P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_gather": [_P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_attn_causal": [_P, _P, _P, _P, _P, _P],
+    "tsa_scatter_residual": [_P, _P, _P, _P, _P, _P, _P],
+    "tsa_layer": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_dense_attn_causal": [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+}
+EXPORTS = ["tsa_status_string", "tsa_check_args", "tsa_capacity", "tsa_stage_workspace_bytes",
+           "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SIGS]
+
+
+def lib():
+    """Open libtsa.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(_LIB_PATH)
+        sp = ctypes.POINTER(Shape)
+        L.tsa_status_string.restype = ctypes.c_char_p
+        L.tsa_status_string.argtypes = [ctypes.c_int]
+        L.tsa_check_args.restype = ctypes.c_int
+        L.tsa_check_args.argtypes = [sp]
+        L.tsa_capacity.restype = ctypes.c_int64
+        L.tsa_capacity.argtypes = [ctypes.c_int64]
+        for n in ("tsa_stage_workspace_bytes", "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes"):
+            getattr(L, n).restype = ctypes.c_size_t
+            getattr(L, n).argtypes = [sp]
+        for n, args in _SIGS.items():
+            getattr(L, n).restype = ctypes.c_int
+            getattr(L, n).argtypes = [sp, *args]
+        _lib = L
+    return _lib
+
+
+def shape(L, Hq, Hkv, d, q, tau, dtype):
+    """A tsa_shape; dtype is "bf16", "f32" or a torch dtype."""
+    if dtype in ("bf16", torch.bfloat16):
+        dt = BF16
+    elif dtype in ("f32", torch.float32):
+        dt = F32
+    else:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return Shape(int(L), int(Hq), int(Hkv), int(d), int(q), float(tau), dt)
+
+
+def shape_of(cfg):
+    return shape(cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.q, cfg.tau, cfg.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    """None: torch's current stream; an int: a raw hipStream_t handle; else a torch stream."""
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise TsaError(fn, status)
+
+
+def check_args(s):
+    return lib().tsa_check_args(ctypes.byref(s))
+
+
+def capacity(L):
+    return lib().tsa_capacity(int(L))
+
+
+def stage_workspace_bytes(s):
+    return lib().tsa_stage_workspace_bytes(ctypes.byref(s))
+
+
+def layer_workspace_bytes(s):
+    return lib().tsa_layer_workspace_bytes(ctypes.byref(s))
+
+
+def dense_workspace_bytes(s):
+    return lib().tsa_dense_workspace_bytes(ctypes.byref(s))
+
+
+def workspace(nbytes, device="cuda"):
+    """A device buffer for the library's workspace (torch's allocator returns 256-byte aligned
+    blocks)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    return _ptr(ws), ctypes.c_size_t(0 if ws is None else ws.numel() * ws.element_size())
+
+
+def score(s, Q, K, s_h, s_l=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_score", lib().tsa_score(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(s_h), _ptr(s_l), p, n,
+                                        _stream(stream)))
+
+
+def budget(s, s_l, k_dev=None, Lp_dev=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_budget", lib().tsa_budget(ctypes.byref(s), _ptr(s_l), _ptr(k_dev), _ptr(Lp_dev), p, n,
+                                          _stream(stream)))
+
+
+def select(s, s_h, Lp_dev, idx, inv=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_select", lib().tsa_select(ctypes.byref(s), _ptr(s_h), _ptr(Lp_dev), _ptr(idx), _ptr(inv),
+                                          p, n, _stream(stream)))
+
+
+def gather(s, Q, K, V, idx, Lp_dev, Qh, Kh, Vht, stream=None):
+    _check("tsa_gather", lib().tsa_gather(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V), _ptr(idx),
+                                          _ptr(Lp_dev), _ptr(Qh), _ptr(Kh), _ptr(Vht), _stream(stream)))
+
+
+def attn_causal(s, Qh, Kh, Vht, Lp_dev, Oh, stream=None):
+    _check("tsa_attn_causal", lib().tsa_attn_causal(ctypes.byref(s), _ptr(Qh), _ptr(Kh), _ptr(Vht),
+                                                    _ptr(Lp_dev), _ptr(Oh), _stream(stream)))
+
+
+def scatter_residual(s, Oh, idx, inv, Lp_dev, X, Y, stream=None):
+    _check("tsa_scatter_residual", lib().tsa_scatter_residual(ctypes.byref(s), _ptr(Oh), _ptr(idx), _ptr(inv),
+                                                              _ptr(Lp_dev), _ptr(X), _ptr(Y), _stream(stream)))
+
+
+def layer(s, Q, K, V, X, Y, kLp_dev=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_layer", lib().tsa_layer(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y),
+                                        _ptr(kLp_dev), p, n, _stream(stream)))
+
+
+def dense_attn_causal(s, Q, K, V, X, Y, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_dense_attn_causal", lib().tsa_dense_attn_causal(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
+                                                                _ptr(X), _ptr(Y), p, n, _stream(stream)))

@@ -1,0 +1,287 @@
+// C ABI of libtsa.so: argument validation (host only, before any launch), workspace carving and
+// the stage-by-stage orchestration of the Token Sparse Attention prefill layer.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "tsa.h"
+#include "tsa_internal.h"
+
+using namespace tsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+size_t elem_bytes(int dtype) { return dtype == TSA_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+hipStream_t stream_of(void* s) { return static_cast<hipStream_t>(s); }
+int hip_status(hipError_t e) { return e == hipSuccess ? TSA_OK : TSA_ERR_HIP; }
+
+// Offsets (bytes) of the stage workspace; each region 256-byte aligned.
+struct StageWs {
+  size_t partials, rowstat, S, tilesum, bhist, bctl, kLp, shist, sctl, tcnt, toff, total;
+};
+
+StageWs stage_layout(const tsa_shape* s) {
+  StageWs w;
+  size_t o = 0;
+  auto take = [&](size_t n) { size_t at = o; o += up(n); return at; };
+  w.partials = take(score_partial_bytes(s->L, s->Hq, s->q));
+  w.rowstat = take((size_t)s->Hq * s->q * sizeof(double2));
+  w.S = take((size_t)s->L * sizeof(double));
+  w.tilesum = take((size_t)layer_tiles(s->L) * sizeof(double));
+  w.bhist = take((size_t)kRadixPasses * 2 * kRadixBins * sizeof(uint64_t));
+  w.bctl = take((size_t)kRadixPasses * sizeof(RadixCtl));
+  w.kLp = take(2 * sizeof(int32_t));
+  w.shist = take((size_t)s->Hq * kRadixPasses * 2 * kRadixBins * sizeof(uint64_t));
+  w.sctl = take((size_t)s->Hq * kRadixPasses * sizeof(RadixCtl));
+  w.tcnt = take((size_t)s->Hq * select_tiles(s->L) * 2 * sizeof(uint32_t));
+  w.toff = take((size_t)s->Hq * select_tiles(s->L) * 2 * sizeof(uint32_t));
+  w.total = o;
+  return w;
+}
+
+// The layer workspace = stage workspace + every intermediate tensor of the layer.
+struct LayerWs {
+  StageWs st;
+  size_t s_h, s_l, idx, inv, Qh, Kh, Vht, Oh, total;
+};
+
+LayerWs layer_layout(const tsa_shape* s) {
+  LayerWs w;
+  w.st = stage_layout(s);
+  size_t o = w.st.total;
+  auto take = [&](size_t n) { size_t at = o; o += up(n); return at; };
+  const size_t C = (size_t)tsa_capacity(s->L);
+  const size_t hl = (size_t)s->Hq * s->L;
+  const size_t comp = (size_t)s->Hq * C * s->d * elem_bytes(s->dtype);
+  w.s_h = take(hl * sizeof(float));
+  w.s_l = take((size_t)s->L * sizeof(float));
+  w.idx = take(hl * sizeof(int32_t));
+  w.inv = take(hl * sizeof(int32_t));
+  w.Qh = take(comp);
+  w.Kh = take(comp);
+  w.Vht = take(comp);
+  w.Oh = take(comp);
+  w.total = o;
+  return w;
+}
+
+template <typename T> T* at(void* base, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(base) + off); }
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (ws == nullptr || ((uintptr_t)ws & (kAlign - 1)) != 0 || have < need) return TSA_ERR_WORKSPACE;
+  return TSA_OK;
+}
+
+#define TSA_TRY(expr)                 \
+  do {                                \
+    const int st_ = (expr);           \
+    if (st_ != TSA_OK) return st_;    \
+  } while (0)
+
+int need_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (p == nullptr) return TSA_ERR_ARG;
+    if (!aligned16(p)) return TSA_ERR_ALIGN;
+  }
+  return TSA_OK;
+}
+
+int opt_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p != nullptr && !aligned16(p)) return TSA_ERR_ALIGN;
+  return TSA_OK;
+}
+
+int need_int_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps) {
+    if (p == nullptr) return TSA_ERR_ARG;
+    if (((uintptr_t)p & 3u) != 0) return TSA_ERR_ALIGN;
+  }
+  return TSA_OK;
+}
+
+uint64_t budget_target(float tau) {
+  // ceil(tau * 2^60): the integer fixed-point mass that "C(j) >= tau" must reach.
+  return (uint64_t)std::ceil(std::ldexp((double)tau, 60));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tsa_status_string(int status) {
+  switch (status) {
+    case TSA_OK: return "ok";
+    case TSA_ERR_ARG: return "invalid argument";
+    case TSA_ERR_SHAPE: return "unsupported shape";
+    case TSA_ERR_DTYPE: return "unsupported dtype";
+    case TSA_ERR_ALIGN: return "tensor not 16-byte aligned";
+    case TSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case TSA_ERR_HIP: return "HIP launch failed";
+    case TSA_ERR_UNSUPPORTED: return "not implemented for these parameters";
+    default: return "unknown status";
+  }
+}
+
+int tsa_check_args(const tsa_shape* s) {
+  if (s == nullptr) return TSA_ERR_ARG;
+  if (s->dtype != TSA_F32 && s->dtype != TSA_BF16) return TSA_ERR_DTYPE;
+  if (!(s->tau >= 0.f && s->tau < 1.f)) return TSA_ERR_ARG;   // also rejects NaN
+  if (s->L < 1 || s->L >= (int64_t(1) << 31)) return TSA_ERR_SHAPE;
+  if (s->Hq < 1 || s->Hkv < 1 || s->Hq > 1024 || s->Hkv > s->Hq || s->Hq % s->Hkv != 0) return TSA_ERR_SHAPE;
+  if (s->q < 1 || s->q > 1024 || (int64_t)s->q > s->L) return TSA_ERR_SHAPE;
+  if (s->d != 64 && s->d != 128) return TSA_ERR_UNSUPPORTED;
+  return TSA_OK;
+}
+
+int64_t tsa_capacity(int64_t L) { return (L + 255) / 256 * 256; }
+
+size_t tsa_stage_workspace_bytes(const tsa_shape* s) {
+  return tsa_check_args(s) == TSA_OK ? stage_layout(s).total : 0;
+}
+
+size_t tsa_layer_workspace_bytes(const tsa_shape* s) {
+  return tsa_check_args(s) == TSA_OK ? layer_layout(s).total : 0;
+}
+
+size_t tsa_dense_workspace_bytes(const tsa_shape* s) {
+  if (tsa_check_args(s) != TSA_OK) return 0;
+  return up((size_t)s->Hkv * s->d * tsa_capacity(s->L) * elem_bytes(s->dtype));
+}
+
+int tsa_score(const tsa_shape* s, const void* Q, const void* K, float* s_h, float* s_l, void* ws,
+              size_t ws_bytes, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Q, K, s_h}));
+  TSA_TRY(opt_ptrs({s_l}));
+  const StageWs w = stage_layout(s);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  hipError_t e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h,
+                              at<double2>(ws, w.partials), at<double2>(ws, w.rowstat), stream_of(stream));
+  if (e == hipSuccess && s_l)
+    e = launch_layer_score(s_h, s->L, s->Hq, at<double>(ws, w.S), at<double>(ws, w.tilesum), s_l,
+                           stream_of(stream));
+  return hip_status(e);
+}
+
+int tsa_budget(const tsa_shape* s, const float* s_l, int32_t* k_dev, int32_t* Lp_dev, void* ws,
+               size_t ws_bytes, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({s_l}));
+  if ((k_dev && ((uintptr_t)k_dev & 3u)) || (Lp_dev && ((uintptr_t)Lp_dev & 3u))) return TSA_ERR_ALIGN;
+  const StageWs w = stage_layout(s);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  hipStream_t st = stream_of(stream);
+  hipError_t e = launch_fill_zero(at<char>(ws, w.bhist), w.kLp - w.bhist, st);
+  if (e == hipSuccess)
+    e = launch_budget(s_l, s->L, budget_target(s->tau), at<uint64_t>(ws, w.bhist), at<RadixCtl>(ws, w.bctl),
+                      at<int32_t>(ws, w.kLp), k_dev, Lp_dev, st);
+  return hip_status(e);
+}
+
+int tsa_select(const tsa_shape* s, const float* s_h, const int32_t* Lp_dev, int32_t* idx, int32_t* inv,
+               void* ws, size_t ws_bytes, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({s_h, idx}));
+  TSA_TRY(opt_ptrs({inv}));
+  TSA_TRY(need_int_ptrs({Lp_dev}));
+  const StageWs w = stage_layout(s);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  hipStream_t st = stream_of(stream);
+  hipError_t e = launch_fill_zero(at<char>(ws, w.shist), w.tcnt - w.shist, st);
+  if (e == hipSuccess)
+    e = launch_select(s_h, s->L, s->Hq, Lp_dev, at<uint64_t>(ws, w.shist), at<RadixCtl>(ws, w.sctl),
+                      at<uint32_t>(ws, w.tcnt), at<uint32_t>(ws, w.toff), idx, inv, st);
+  return hip_status(e);
+}
+
+int tsa_gather(const tsa_shape* s, const void* Q, const void* K, const void* V, const int32_t* idx,
+               const int32_t* Lp_dev, void* Qh, void* Kh, void* Vht, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Q, K, V, idx, Qh, Kh, Vht}));
+  TSA_TRY(need_int_ptrs({Lp_dev}));
+  return hip_status(launch_gather(s->dtype, s->d, Q, K, V, idx, Lp_dev, s->L, s->Hq, s->Hkv,
+                                  tsa_capacity(s->L), Qh, Kh, Vht, stream_of(stream)));
+}
+
+int tsa_attn_causal(const tsa_shape* s, const void* Qh, const void* Kh, const void* Vht,
+                    const int32_t* Lp_dev, void* Oh, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Qh, Kh, Vht, Oh}));
+  TSA_TRY(need_int_ptrs({Lp_dev}));
+  return hip_status(launch_attention(s->dtype, s->d, false, Qh, Kh, Vht, Lp_dev, s->L, s->Hq, s->Hkv,
+                                     tsa_capacity(s->L), nullptr, Oh, stream_of(stream)));
+}
+
+int tsa_scatter_residual(const tsa_shape* s, const void* Oh, const int32_t* idx, const int32_t* inv,
+                         const int32_t* Lp_dev, const void* X, void* Y, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Oh, Y}));
+  TSA_TRY(opt_ptrs({X, inv}));
+  if (inv == nullptr) {
+    TSA_TRY(need_ptrs({idx}));
+    TSA_TRY(need_int_ptrs({Lp_dev}));
+  }
+  return hip_status(launch_scatter(s->dtype, s->d, Oh, idx, inv, Lp_dev, X, Y, s->L, s->Hq,
+                                   tsa_capacity(s->L), stream_of(stream)));
+}
+
+int tsa_layer(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X, void* Y,
+              int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Q, K, V, Y}));
+  TSA_TRY(opt_ptrs({X}));
+  if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
+  const LayerWs w = layer_layout(s);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  hipStream_t st = stream_of(stream);
+  const StageWs& g = w.st;
+  const int64_t C = tsa_capacity(s->L);
+  float* s_h = at<float>(ws, w.s_h);
+  float* s_l = at<float>(ws, w.s_l);
+  int32_t* kLp = at<int32_t>(ws, g.kLp);
+  int32_t* idx = at<int32_t>(ws, w.idx);
+  int32_t* inv = at<int32_t>(ws, w.inv);
+  hipError_t e = launch_fill_zero(at<char>(ws, g.bhist), g.kLp - g.bhist, st);
+  if (e == hipSuccess) e = launch_fill_zero(at<char>(ws, g.shist), g.tcnt - g.shist, st);
+  if (e == hipSuccess)
+    e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h, at<double2>(ws, g.partials),
+                     at<double2>(ws, g.rowstat), st);
+  if (e == hipSuccess) e = launch_layer_score(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l, st);
+  if (e == hipSuccess)
+    e = launch_budget(s_l, s->L, budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl), kLp,
+                      kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
+  if (e == hipSuccess)
+    e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
+                      at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
+  if (e == hipSuccess)
+    e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C, at<void>(ws, w.Qh),
+                      at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
+  if (e == hipSuccess)
+    e = launch_attention(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
+                         kLp + 1, s->L, s->Hq, s->Hkv, C, nullptr, at<void>(ws, w.Oh), st);
+  if (e == hipSuccess)
+    e = launch_scatter(s->dtype, s->d, at<void>(ws, w.Oh), idx, inv, kLp + 1, X, Y, s->L, s->Hq, C, st);
+  return hip_status(e);
+}
+
+int tsa_dense_attn_causal(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X,
+                          void* Y, void* ws, size_t ws_bytes, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Q, K, V, Y}));
+  TSA_TRY(opt_ptrs({X}));
+  TSA_TRY(check_ws(ws, ws_bytes, tsa_dense_workspace_bytes(s)));
+  hipStream_t st = stream_of(stream);
+  const int64_t C = tsa_capacity(s->L);
+  hipError_t e = launch_transpose_v(s->dtype, s->d, V, s->L, s->Hkv, C, ws, st);
+  if (e == hipSuccess)
+    e = launch_attention(s->dtype, s->d, true, Q, K, ws, nullptr, s->L, s->Hq, s->Hkv, C, X, Y, st);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+// Compress and decompress (papernotes.org reading notes, "Key design 1"; bxzpzcl.cn article,
+// section 1.1 gather / zeros_like + scatter_): pure data movement in 16-byte vectors.
+//
+// gather : per query head, rows idx[h][0..L') of Q, K, V -> dense Qh, Kh [Hq][C][d] and the
+//          transposed Vht [Hq][d][C] (a 64-row tile is staged in LDS and written column-major so
+//          the stores stay contiguous).
+// scatter: Y[t][h] = X[t][h] + Oh[h][inv[h][t]] for selected t, X[t][h] otherwise (float32 sum,
+//          one rounding); without X the selected rows are copied and the others are +0.0.
+#include "kern_common.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+
+constexpr int kTileRows = 64;
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, const T* __restrict__ K,
+                                                     const T* __restrict__ V, const int32_t* __restrict__ idx,
+                                                     const int32_t* __restrict__ Lp_dev, int64_t L, int Hq,
+                                                     int Hkv, int64_t C, T* __restrict__ Qh,
+                                                     T* __restrict__ Kh, T* __restrict__ Vht) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;     // 16-byte vectors per row
+  constexpr int EPV = 16 / (int)sizeof(T);         // elements per vector
+  __shared__ uint4 stage[kTileRows * VPR];
+  const int h = blockIdx.y, g = h / (Hq / Hkv);
+  const int64_t i0 = (int64_t)blockIdx.x * kTileRows;
+  const int64_t Lp = Lp_dev[0];
+  if (i0 >= Lp) return;
+  const int n = (int)(Lp - i0 < kTileRows ? Lp - i0 : kTileRows);
+  const uint4* Q4 = reinterpret_cast<const uint4*>(Q);
+  const uint4* K4 = reinterpret_cast<const uint4*>(K);
+  const uint4* V4 = reinterpret_cast<const uint4*>(V);
+  uint4* Qh4 = reinterpret_cast<uint4*>(Qh);
+  uint4* Kh4 = reinterpret_cast<uint4*>(Kh);
+  for (int e = threadIdx.x; e < kTileRows * VPR; e += 256) {
+    const int r = e / VPR, c = e % VPR;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < n) {
+      const int64_t t = idx[(size_t)h * L + i0 + r];
+      const size_t dst = ((size_t)h * C + i0 + r) * VPR + c;
+      Qh4[dst] = Q4[((size_t)t * Hq + h) * VPR + c];
+      Kh4[dst] = K4[((size_t)t * Hkv + g) * VPR + c];
+      v = V4[((size_t)t * Hkv + g) * VPR + c];
+    }
+    stage[e] = v;
+  }
+  __syncthreads();
+  // Vht[h][dd][i0 + j .. i0 + j + EPV): gather EPV consecutive rows of column dd from the stage.
+  const T* st = reinterpret_cast<const T*>(stage);
+  for (int e = threadIdx.x; e < D * (kTileRows / EPV); e += 256) {
+    const int dd = e / (kTileRows / EPV), j0 = (e % (kTileRows / EPV)) * EPV;
+    T vals[EPV];
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) vals[u] = st[(j0 + u) * D + dd];
+    uint4 w;
+    __builtin_memcpy(&w, vals, 16);
+    *reinterpret_cast<uint4*>(Vht + ((size_t)h * D + dd) * C + i0 + j0) = w;
+  }
+}
+
+// V [L][Hkv][d] -> Vt [Hkv][d][C], columns L .. C-1 zero (the dense path's value layout).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void transpose_v_kernel(const T* __restrict__ V, int64_t L, int Hkv,
+                                                          int64_t C, T* __restrict__ Vt) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  constexpr int EPV = 16 / (int)sizeof(T);
+  __shared__ uint4 stage[kTileRows * VPR];
+  const int g = blockIdx.y;
+  const int64_t t0 = (int64_t)blockIdx.x * kTileRows;
+  const uint4* V4 = reinterpret_cast<const uint4*>(V);
+  for (int e = threadIdx.x; e < kTileRows * VPR; e += 256) {
+    const int r = e / VPR, c = e % VPR;
+    stage[e] = t0 + r < L ? V4[((size_t)(t0 + r) * Hkv + g) * VPR + c] : make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();
+  const T* st = reinterpret_cast<const T*>(stage);
+  for (int e = threadIdx.x; e < D * (kTileRows / EPV); e += 256) {
+    const int dd = e / (kTileRows / EPV), j0 = (e % (kTileRows / EPV)) * EPV;
+    T vals[EPV];
+#pragma unroll
+    for (int u = 0; u < EPV; ++u) vals[u] = st[(j0 + u) * D + dd];
+    uint4 w;
+    __builtin_memcpy(&w, vals, 16);
+    *reinterpret_cast<uint4*>(Vt + ((size_t)g * D + dd) * C + t0 + j0) = w;
+  }
+}
+
+// x + o on one 16-byte vector, float32 sum rounded once to the storage type.
+template <typename T>
+__device__ __forceinline__ uint4 add_vec(uint4 x, uint4 o) {
+  uint4 y;
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t xa[4] = {x.x, x.y, x.z, x.w}, oa[4] = {o.x, o.y, o.z, o.w};
+    uint32_t ya[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_to_f32((uint16_t)xa[j]) + bf16_to_f32((uint16_t)oa[j]);
+      const float hi = bf16_to_f32((uint16_t)(xa[j] >> 16)) + bf16_to_f32((uint16_t)(oa[j] >> 16));
+      ya[j] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    }
+    y = make_uint4(ya[0], ya[1], ya[2], ya[3]);
+  } else {
+    y.x = __float_as_uint(__uint_as_float(x.x) + __uint_as_float(o.x));
+    y.y = __float_as_uint(__uint_as_float(x.y) + __uint_as_float(o.y));
+    y.z = __float_as_uint(__uint_as_float(x.z) + __uint_as_float(o.z));
+    y.w = __float_as_uint(__uint_as_float(x.w) + __uint_as_float(o.w));
+  }
+  return y;
+}
+
+// Token-major pass over Y using the inverse map: every (t, h) row is produced exactly once.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ Oh, const int32_t* __restrict__ inv,
+                                                          const T* X, T* Y, int64_t L, int Hq, int64_t C) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  const uint4* O4 = reinterpret_cast<const uint4*>(Oh);
+  const uint4* X4 = reinterpret_cast<const uint4*>(X);
+  uint4* Y4 = reinterpret_cast<uint4*>(Y);
+  const bool alias = (const void*)X == (const void*)Y;
+  const size_t n = (size_t)L * Hq * VPR;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    const size_t th = e / VPR;
+    const int c = (int)(e % VPR);
+    const int h = (int)(th % Hq);
+    const int64_t t = (int64_t)(th / Hq);
+    const int32_t j = inv[(size_t)h * L + t];
+    if (j < 0) {
+      if (alias) continue;
+      Y4[e] = X4 ? X4[e] : make_uint4(0, 0, 0, 0);
+    } else {
+      const uint4 o = O4[((size_t)h * C + j) * VPR + c];
+      Y4[e] = X4 ? add_vec<T>(X4[e], o) : o;
+    }
+  }
+}
+
+// Index-driven variant (no inverse map): Y must already hold X (or zeros for a pure decompress).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void scatter_idx_kernel(const T* __restrict__ Oh, const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ Lp_dev, bool add,
+                                                          T* Y, int64_t L, int Hq, int64_t C) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  const int64_t Lp = Lp_dev[0];
+  const uint4* O4 = reinterpret_cast<const uint4*>(Oh);
+  uint4* Y4 = reinterpret_cast<uint4*>(Y);
+  const size_t n = (size_t)Hq * Lp * VPR;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    const int c = (int)(e % VPR);
+    const size_t hi = e / VPR;
+    const int h = (int)(hi / Lp);
+    const int64_t i = (int64_t)(hi % Lp);
+    const int64_t t = idx[(size_t)h * L + i];
+    const size_t dst = ((size_t)t * Hq + h) * VPR + c;
+    const uint4 o = O4[((size_t)h * C + i) * VPR + c];
+    Y4[dst] = add ? add_vec<T>(Y4[dst], o) : o;
+  }
+}
+
+__global__ void copy16_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+static unsigned grid_for(size_t n) {
+  const size_t b = (n + 255) / 256;
+  return (unsigned)(b < 16384 ? (b ? b : 1) : 16384);
+}
+
+template <typename T, int D>
+static hipError_t run_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
+                             const int32_t* Lp_dev, int64_t L, int Hq, int Hkv, int64_t C, void* Qh,
+                             void* Kh, void* Vht, hipStream_t st) {
+  const dim3 grid((unsigned)((L + kTileRows - 1) / kTileRows), (unsigned)Hq);
+  gather_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(Q), static_cast<const T*>(K),
+                                            static_cast<const T*>(V), idx, Lp_dev, L, Hq, Hkv, C,
+                                            static_cast<T*>(Qh), static_cast<T*>(Kh), static_cast<T*>(Vht));
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(int dtype, int d, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
+                         int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st) {
+  if (dtype == 1)
+    return d == 128 ? run_gather<uint16_t, 128>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st)
+                    : run_gather<uint16_t, 64>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st);
+  return d == 128 ? run_gather<float, 128>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st)
+                  : run_gather<float, 64>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st);
+}
+
+template <typename T, int D>
+static hipError_t run_transpose(const void* V, int64_t L, int Hkv, int64_t C, void* Vt, hipStream_t st) {
+  const dim3 grid((unsigned)(C / kTileRows), (unsigned)Hkv);
+  transpose_v_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(V), L, Hkv, C, static_cast<T*>(Vt));
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_v(int dtype, int d, const void* V, int64_t L, int Hkv, int64_t C,
+                              void* Vt, hipStream_t st) {
+  if (dtype == 1)
+    return d == 128 ? run_transpose<uint16_t, 128>(V, L, Hkv, C, Vt, st)
+                    : run_transpose<uint16_t, 64>(V, L, Hkv, C, Vt, st);
+  return d == 128 ? run_transpose<float, 128>(V, L, Hkv, C, Vt, st)
+                  : run_transpose<float, 64>(V, L, Hkv, C, Vt, st);
+}
+
+template <typename T, int D>
+static hipError_t run_scatter(const void* Oh, const int32_t* idx, const int32_t* inv,
+                              const int32_t* Lp_dev, const void* X, void* Y, int64_t L, int Hq,
+                              int64_t C, hipStream_t st) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  const size_t n = (size_t)L * Hq * VPR;
+  if (inv) {
+    scatter_inv_kernel<T, D><<<grid_for(n), 256, 0, st>>>(static_cast<const T*>(Oh), inv,
+                                                          static_cast<const T*>(X), static_cast<T*>(Y), L, Hq, C);
+    return hipGetLastError();
+  }
+  if (X == nullptr) {
+    hipError_t e = launch_fill_zero(Y, n * 16, st);
+    if (e != hipSuccess) return e;
+  } else if (X != Y) {
+    copy16_kernel<<<grid_for(n), 256, 0, st>>>(static_cast<const uint4*>(X), static_cast<uint4*>(Y), n);
+  }
+  scatter_idx_kernel<T, D><<<grid_for(n), 256, 0, st>>>(static_cast<const T*>(Oh), idx, Lp_dev, X != nullptr,
+                                                        static_cast<T*>(Y), L, Hq, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(int dtype, int d, const void* Oh, const int32_t* idx, const int32_t* inv,
+                          const int32_t* Lp_dev, const void* X, void* Y, int64_t L, int Hq, int64_t C,
+                          hipStream_t st) {
+  if (dtype == 1)
+    return d == 128 ? run_scatter<uint16_t, 128>(Oh, idx, inv, Lp_dev, X, Y, L, Hq, C, st)
+                    : run_scatter<uint16_t, 64>(Oh, idx, inv, Lp_dev, X, Y, L, Hq, C, st);
+  return d == 128 ? run_scatter<float, 128>(Oh, idx, inv, Lp_dev, X, Y, L, Hq, C, st)
+                  : run_scatter<float, 64>(Oh, idx, inv, Lp_dev, X, Y, L, Hq, C, st);
+}
+
+}  // namespace tsa

@@ -1,0 +1,61 @@
+// Internal interface between the C ABI (api.cpp) and the kernel launchers (*.hip).
+// Every launcher enqueues on `st` and returns hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tsa {
+
+// Per-pass control word of a radix select over one segment (see select.hip).
+struct RadixCtl {
+  uint32_t prefix;      // key bits fixed so far (high bits first)
+  uint32_t none;        // 1: the target exceeds the segment's total weight
+  uint64_t cnt_below;   // elements whose key is below the current prefix range
+  uint64_t w_below;     // their total weight
+  uint64_t n_bin;       // elements in the chosen bucket of the last pass
+};
+
+constexpr int kRadixBins = 256;
+constexpr int kRadixPasses = 4;
+
+// ---- score.hip ----------------------------------------------------------------------------------
+// Rows scored per KV group: R = (Hq/Hkv) * q; blocks of 256 keys; 4 waves per block.
+int64_t score_blocks(int64_t L);
+size_t score_partial_bytes(int64_t L, int Hq, int q);
+hipError_t launch_score(int dtype, int d, const void* Q, const void* K, int64_t L, int Hq, int Hkv,
+                        int q, float* s_h, double2* partials, double2* rowstat, hipStream_t st);
+
+// ---- select.hip ---------------------------------------------------------------------------------
+int64_t layer_tiles(int64_t L);
+hipError_t launch_layer_score(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum,
+                              float* s_l, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// Budget over s_l: writes k and L' (either may be null) and keeps them in kLp_ws[0..1].
+hipError_t launch_budget(const float* s_l, int64_t L, uint64_t target, uint64_t* hist,
+                         RadixCtl* ctl, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
+                         hipStream_t st);
+int64_t select_tiles(int64_t L);
+hipError_t launch_select(const float* s_h, int64_t L, int Hq, const int32_t* Lp_dev,
+                         uint64_t* hist, RadixCtl* ctl, uint32_t* tile_cnt, uint32_t* tile_off,
+                         int32_t* idx, int32_t* inv, hipStream_t st);
+
+// ---- move.hip -----------------------------------------------------------------------------------
+hipError_t launch_gather(int dtype, int d, const void* Q, const void* K, const void* V,
+                         const int32_t* idx, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
+                         int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st);
+hipError_t launch_transpose_v(int dtype, int d, const void* V, int64_t L, int Hkv, int64_t C,
+                              void* Vt, hipStream_t st);
+hipError_t launch_scatter(int dtype, int d, const void* Oh, const int32_t* idx, const int32_t* inv,
+                          const int32_t* Lp_dev, const void* X, void* Y, int64_t L, int Hq,
+                          int64_t C, hipStream_t st);
+
+// ---- attention.hip ------------------------------------------------------------------------------
+// Compressed (dense == false): Qh/Kh [Hq][C][d], Vht [Hq][d][C], L' from Lp_dev, output Oh.
+// Dense (dense == true): Q [L][Hq][d], K [L][Hkv][d], Vt [Hkv][d][C] (C >= L), output
+// Y [L][Hq][d] = X + O (X may be null).
+hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const void* K,
+                            const void* Vt, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
+                            int64_t C, const void* X, void* O, hipStream_t st);
+
+}  // namespace tsa
