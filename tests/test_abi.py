@@ -121,3 +121,12 @@ def test_select_sparse_layers_rule():
     cfg = CONFIGS[5]
     assert select_sparse_layers(chain_drift_values(cfg)) == list(cfg.sparse_layers)
     assert select_sparse_layers([0.3, 0.1, 0.2, 0.1]) == [2, 4]
+
+
+def test_every_kernel_has_its_host_launch_stub():
+    """A kernel whose host-side stub the compiler dropped would fail to load at run time; catch it
+    on the CPU: the library may not leave any __device_stub__ symbol undefined."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", binding._LIB_PATH], capture_output=True, text=True)
+    assert out.returncode == 0, out.stderr
+    assert "__device_stub__" not in out.stdout

@@ -63,18 +63,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 0x0F70: wait until every vector-memory load of this wave (including LDS-direct loads) is done.
+#define TSA_WAIT_VMEM() __builtin_amdgcn_s_waitcnt(0x0F70)
+
+// N direct loads of 1 KiB each (16 bytes per lane) from [base, base + bytes) at voff[i] into LDS
+// at lds + 1024*i; bytes past the end arrive as zeros.  The kernel's lambdas are host+device, so
+// the LDS address-space cast (not valid in host code) is compiled in the device pass only;
+// otherwise the host pass silently drops the kernel's launch stub.
+template <int N>
+__host__ __device__ __forceinline__ void dma_1k(const void* base, uint32_t bytes, char* lds, const uint32_t (&voff)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(lds + 1024 * i), 16, voff[i], 0, 0, 0);
+#endif
+}
+
 template <int D, bool DENSE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KS = D / 16;          // K-steps of 16 over the head dim (score product)
-  constexpr int DT = D / 32;          // 32-row tiles of O^T over the head dim
-  constexpr int KLD = D + 8;          // LDS row pitch (elements) of the K tile
-  constexpr int VLD = BN + 8;         // LDS row pitch of the V^T tile
-  constexpr int KCPR = D / 8;         // 16-byte chunks per K row
-  constexpr int KCH = BN * KCPR / 256;    // chunks per thread per K tile
-  constexpr int VCH = D * (BN / 8) / 256; // chunks per thread per V^T tile
-  __shared__ __attribute__((aligned(16))) uint16_t smK[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t smV[2][D * VLD];
+  constexpr int KS = D / 16;            // K-steps of 16 over the head dim (score product)
+  constexpr int DT = D / 32;            // 32-row tiles of O^T over the head dim
+  constexpr int KROW = D * 2;           // bytes per K row in LDS (no padding; XOR-swizzled)
+  constexpr int KTILE = BN * KROW;
+  constexpr int VROW = BN * 2;          // bytes per V^T row in LDS
+  constexpr int VTILE = D * VROW;
+  constexpr int KDMA = KTILE / 1024 / 4;  // 1 KiB direct loads per wave per K tile
+  constexpr int VDMA = VTILE / 1024 / 4;
+  constexpr int NS = 2 * KS, EPC = 32 / NS, NV = 4 * DT, PF = 2;
+  // LDS: K slots 0,1 then V slots 0,1
+  __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * VTILE];
 
   const int nmb = (int)((a.L + BM - 1) / BM);
   int h, mb;
@@ -83,9 +104,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int m0 = mb * BM;
   if (m0 >= Lp) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = h / (a.Hq / a.Hkv);
-  // per-head bases (bytes) and row pitches
   const uint32_t q_rs = DENSE ? a.Hq * D * 2 : D * 2;
   const uint32_t k_rs = DENSE ? a.Hkv * D * 2 : D * 2;
   const uint32_t v_rs = (uint32_t)a.C * 2;
@@ -93,7 +114,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const char* kbase = static_cast<const char*>(a.K) + (DENSE ? (size_t)g * D * 2 : (size_t)h * a.C * D * 2);
   const char* vbase = static_cast<const char*>(a.Vt) + (size_t)(DENSE ? g : h) * D * a.C * 2;
 
-  const int qi = m0 + 32 * w + ln;    // this lane's query row
+  const int qi = m0 + 32 * w + ln;      // this lane's query row
   bf16x8_t qf[KS];
   {
     const char* qrow = qbase + (size_t)qi * q_rs + (D / 2) * hf * 2;
@@ -101,110 +122,88 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int s = 0; s < KS; ++s)
       qf[s] = qi < Lp ? *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s) : bf16x8_t{};
   }
-
   const int kend = m0 + BM < Lp ? m0 + BM : Lp;
   const int nkb = (kend + BN - 1) / BN;
 
-  uint32_t voff_k[KCH], voff_v[VCH];
+  // Tile layouts.  K: LDS row m holds key perm(m) (bits 2 and 3 of the key swapped), 16-byte chunk
+  // c of a row sits in slot c ^ kswz(m).  V^T: row = head-dim index, chunk c (keys 8c..8c+7) in
+  // slot c ^ vswz(row).  Both swizzles leave every 8 and every 16 consecutive rows' reads of one
+  // chunk on distinct banks, and depend only on the row's low 4 bits.
+  auto perm = [](int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); };
+  auto kswz = [](int m) { return KROW == 256 ? (m & 15) : ((m ^ ((m >> 3) & 1)) & 7); };
+  auto vswz = [](int r) { return (r ^ ((r >> 3) & 1)) & 7; };
+
+  // direct-load sources: lane offsets of the chunk each lane brings into its 16-byte LDS slot
+  uint32_t voffK[KDMA], voffV[VDMA];
 #pragma unroll
-  for (int u = 0; u < KCH; ++u) {
-    const int e = tid + 256 * u;
-    voff_k[u] = (uint32_t)(e / KCPR) * k_rs + (uint32_t)(e % KCPR) * 16u;
+  for (int i = 0; i < KDMA; ++i) {
+    const int o = (w * KDMA + i) * 1024 + 16 * lane, m = o / KROW, c = ((o % KROW) / 16) ^ kswz(m);
+    voffK[i] = (uint32_t)perm(m) * k_rs + (uint32_t)c * 16u;
   }
 #pragma unroll
-  for (int u = 0; u < VCH; ++u) {
-    const int e = tid + 256 * u;
-    voff_v[u] = (uint32_t)(e / (BN / 8)) * v_rs + (uint32_t)(e % (BN / 8)) * 16u;
+  for (int i = 0; i < VDMA; ++i) {
+    const int o = (w * VDMA + i) * 1024 + 16 * lane, r = o / VROW, c = ((o % VROW) / 16) ^ vswz(r);
+    voffV[i] = (uint32_t)r * v_rs + (uint32_t)c * 16u;
   }
+  auto dma_k = [&](int kb, int slot) {
+    const int key0 = kb * BN, nval = Lp - key0 < BN ? Lp - key0 : BN;
+    // K rows at or beyond L' fall outside the range and arrive as zeros
+    dma_1k<KDMA>(kbase + (size_t)key0 * k_rs, (uint32_t)(nval - 1) * k_rs + D * 2, smem + slot * KTILE + w * KDMA * 1024, voffK);
+  };
+  auto dma_v = [&](int kb, int slot) {
+    dma_1k<VDMA>(vbase + (size_t)kb * BN * 2, (uint32_t)(D - 1) * v_rs + BN * 2, smem + 2 * KTILE + slot * VTILE + w * VDMA * 1024, voffV);
+  };
+  // LDS read offsets (bytes, within a slot) of this lane's fragments; the 32-row sub-tile is an
+  // immediate offset on top
+  uint32_t kaddr[KS], vaddr[4];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = ln * KROW + ((((D / 16) * hf) + ks) ^ kswz(ln)) * 16;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) vaddr[ks] = ln * VROW + ((2 * ks + hf) ^ vswz(ln)) * 16;
 
   f32x16_t o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x16_t{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale * kLog2e;
-  const int wrow0 = m0 + 32 * w;      // first query row of this wave
+  const int wrow0 = m0 + 32 * w;        // first query row of this wave
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // S^T tile of key tile kb from the K slot it lives in (scores of this lane's query, unmasked)
-  auto scores = [&](int slot, f32x16_t (&s)[2]) {
+  auto scores_into = [&](const char* kslot, f32x16_t (&s)[2]) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      s[t] = f32x16_t{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(&smK[slot][(32 * t + ln) * KLD + (D / 2) * hf + 8 * ks]);
-        s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], s[t], 0, 0, 0);
-      }
+    for (int f = 0; f < NS; ++f) {
+      const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kslot + (f & 1) * 32 * KROW + kaddr[f >> 1]);
+      s[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[f >> 1], s[f & 1], 0, 0, 0);
     }
   };
 
-  // Software pipeline: while the softmax of tile kb runs on the vector ALU, the matrix cores already
-  // form the scores of tile kb+1.  K runs one tile ahead of V in LDS (both double-buffered):
-  //   iteration kb reads K(kb+1) from slot (kb+1)&1 and V(kb) from slot kb&1, then stores the
-  //   prefetched K(kb+2) into slot kb&1 and V(kb+1) into slot (kb+1)&1 before the barrier.
-  u32x4_t pk[KCH], pv[VCH];
-  auto load_k = [&](int kb) {
-    const int key0 = kb * BN;
-    const int nval = Lp - key0 < BN ? Lp - key0 : BN;
-    // K rows at or beyond L' fall outside the descriptor and read as zero
-    const auto rk = buffer_rsrc(kbase + (size_t)key0 * k_rs, (uint32_t)(nval - 1) * k_rs + D * 2);
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) pk[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, voff_k[u], 0, 0);
-  };
-  auto load_v = [&](int kb) {
-    const int key0 = kb * BN;
-    const int nval = Lp - key0 < BN ? Lp - key0 : BN;
-    const auto rv = buffer_rsrc(vbase + (size_t)key0 * 2, (uint32_t)(D - 1) * v_rs + BN * 2);
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) pv[u] = __builtin_amdgcn_raw_buffer_load_b128(rv, voff_v[u], 0, 0);
-    if (nval < BN) {                   // last tile: zero the V^T columns at and beyond L'
-#pragma unroll
-      for (int u = 0; u < VCH; ++u) {
-        const int c0 = ((tid + 256 * u) % (BN / 8)) * 8;
-#pragma unroll
-        for (int x = 0; x < 8; ++x)
-          if (c0 + x >= nval) pv[u][x >> 1] &= (x & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      }
-    }
-  };
-  // Key j of a tile goes to LDS row perm(j), which swaps bits 2 and 3 of j.  The score product's
-  // output row 8*(r/4) + 4*hf + r%4 then holds key 16*(r/8) + 8*hf + r%8 (within each 32-key half),
-  // so the 8 probabilities a lane feeds to one value-product step are 8 consecutive keys and its
-  // V^T operand is one contiguous 16-byte LDS read.
-  auto perm = [](int j) { return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1); };
-  auto store_k = [&](int slot) {
-#pragma unroll
-    for (int u = 0; u < KCH; ++u) {
-      const int e = tid + 256 * u;
-      *reinterpret_cast<u32x4_t*>(&smK[slot][perm(e / KCPR) * KLD + 8 * (e % KCPR)]) = pk[u];
-    }
-  };
-  auto store_v = [&](int slot) {
-#pragma unroll
-    for (int u = 0; u < VCH; ++u) {
-      const int e = tid + 256 * u;
-      *reinterpret_cast<u32x4_t*>(&smV[slot][(e / (BN / 8)) * VLD + 8 * (e % (BN / 8))]) = pv[u];
-    }
-  };
-
-  load_k(0);
-  load_v(0);
-  store_k(0);
-  store_v(0);
-  if (nkb > 1) {
-    load_k(1);
-    store_k(1);
-  }
+  dma_k(0, 0);
+  dma_v(0, 0);
+  if (nkb > 1) dma_k(1, 1);
+  TSA_WAIT_VMEM();
   __syncthreads();
-  f32x16_t sc[2];
-  scores(0, sc);
-  __syncthreads();                    // K slot 0 is refilled at the end of iteration 0
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + 2 < nkb) load_k(kb + 2);
-    if (kb + 1 < nkb) load_v(kb + 1);
-    const int key0 = kb * BN;
-    // Diagonal (or, for this wave, fully masked) tile: keys after the query get -inf.  Every
-    // wave's first tile has a visible key, so the running max is finite from tile 0 on.
+  f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+  scores_into(smem, sc);
+  __syncthreads();                      // K slot 0 is refilled at the start of iteration 0
+
+  // One tile.  K runs one tile ahead of V: iteration kb reads K(kb+1) from slot (kb+1)&1 and V(kb)
+  // from slot kb&1; at its start it directs K(kb+2) into slot kb&1 and V(kb+1) into slot (kb+1)&1,
+  // whose previous contents every wave finished with before the last barrier.
+  auto tile = [&](int kb, int P) {     // P = kb & 1, a literal at both call sites
+    const char* kslot = smem + (P ^ 1) * KTILE;
+    const char* vslot = smem + 2 * KTILE + P * VTILE;
+    if (kb + 2 < nkb) dma_k(kb + 2, P);
+    if (kb + 1 < nkb) dma_v(kb + 1, P ^ 1);
+    const int key0 = kb * BN, nval = Lp - key0;
+    if (nval < BN) {                    // last tile: zero the V^T columns at and beyond L'
+      for (int e = tid; e < D * (BN - nval); e += 256) {
+        const int r = e / (BN - nval), col = nval + e % (BN - nval);
+        *reinterpret_cast<uint16_t*>(const_cast<char*>(vslot) + r * VROW + (((col >> 3) ^ vswz(r)) << 4) + (col & 7) * 2) = 0;
+      }
+      __syncthreads();
+    }
+    // diagonal (or, for this wave, fully masked) tile: keys after the query get -inf; every
+    // wave's first tile has a visible key, so the running max is finite from tile 0 on
     if (key0 + BN - 1 > wrow0) {
       const int rel = qi - key0 - 8 * hf;
 #pragma unroll
@@ -227,29 +226,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       m_run = mx;
     }
     const float mb2 = m_run * sl2;
-    // The next tile's score product (2*KS MFMAs) is issued in program order interleaved with this
-    // tile's exponentials, EPC elements per MFMA, so the vector ALU works while the matrix cores
-    // run; then the value product (4*DT MFMAs).  LDS fragments are read PF chunks ahead; the
-    // sched_barrier fences keep the compiler from regrouping the chunks.  (On the last tile the
-    // next-score product reads a stale slot and is discarded.)
-    constexpr int NS = 2 * KS, EPC = 32 / NS, PF = 2, NV = 4 * DT;
-    const uint16_t* kslot = smK[(kb + 1) & 1];
-    const uint16_t* vslot = smV[kb & 1];
-    auto kfrag = [&](int f) {          // f = 2*ks + t
-      return *reinterpret_cast<const bf16x8_t*>(kslot + (32 * (f & 1) + ln) * KLD + (D / 2) * hf + 8 * (f >> 1));
-    };
-    auto vfrag = [&](int f) {          // f = DT*ks + dt: keys 16*ks + 8*hf .. +7 of head-dim row dt
-      return *reinterpret_cast<const bf16x8_t*>(vslot + (32 * (f % DT) + ln) * VLD + 16 * (f / DT) + 8 * hf);
-    };
+    // next tile's score MFMAs issued in program order with this tile's exponentials (EPC per MFMA),
+    // then the value MFMAs; LDS fragments read PF steps ahead; fences keep the order.  (On the last
+    // tile the next-score product reads a stale slot and is discarded.)
     f32x16_t sn[2] = {f32x16_t{}, f32x16_t{}};
     bf16x8_t pb[4];
     bf16x8_t kf[PF + 1], vf[PF + 1];
+    auto kfrag = [&](int f) { return *reinterpret_cast<const bf16x8_t*>(kslot + (f & 1) * 32 * KROW + kaddr[f >> 1]); };
+    auto vfrag = [&](int f) { return *reinterpret_cast<const bf16x8_t*>(vslot + (f % DT) * 32 * VROW + vaddr[f / DT]); };
 #pragma unroll
     for (int f = 0; f < PF; ++f) kf[f] = kfrag(f);
 #pragma unroll
     for (int f = 0; f < NS; ++f) {
       if (f + PF < NS) kf[(f + PF) % (PF + 1)] = kfrag(f + PF);
-      else if (f + PF - NS < PF) vf[f + PF - NS] = vfrag(f + PF - NS);
+      else vf[f + PF - NS] = vfrag(f + PF - NS);
       sn[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f % (PF + 1)], qf[f >> 1], sn[f & 1], 0, 0, 0);
 #pragma unroll
       for (int x = 0; x < EPC; x += 2) {
@@ -269,12 +259,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       o[f % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (PF + 1)], pb[f / DT], o[f % DT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kb + 2 < nkb) store_k(kb & 1);
-    if (kb + 1 < nkb) store_v((kb + 1) & 1);
+    TSA_WAIT_VMEM();
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 2; ++t) sc[t] = sn[t];
+  };
+  int kb = 0;
+  for (; kb + 1 < nkb; kb += 2) {
+    tile(kb, 0);
+    tile(kb + 1, 1);
   }
+  if (kb < nkb) tile(kb, 0);
 
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (qi >= Lp) return;
