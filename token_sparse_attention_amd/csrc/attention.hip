@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int VTILE = D * VROW;
   constexpr int KDMA = KTILE / 1024 / 4;  // 1 KiB direct loads per wave per K tile
   constexpr int VDMA = VTILE / 1024 / 4;
-  constexpr int NS = 2 * KS, EPC = 32 / NS, NV = 4 * DT, PF = 2;
+  constexpr int NS = 2 * KS, NV = 4 * DT, PF = 3;
   // LDS: K slots 0,1 then V slots 0,1
   __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * VTILE];
 
@@ -231,19 +231,32 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // tile the next-score product reads a stale slot and is discarded.)
     f32x16_t sn[2] = {f32x16_t{}, f32x16_t{}};
     bf16x8_t pb[4];
-    bf16x8_t kf[PF + 1], vf[PF + 1];
-    auto kfrag = [&](int f) { return *reinterpret_cast<const bf16x8_t*>(kslot + (f & 1) * 32 * KROW + kaddr[f >> 1]); };
-    auto vfrag = [&](int f) { return *reinterpret_cast<const bf16x8_t*>(vslot + (f % DT) * 32 * VROW + vaddr[f / DT]); };
+    // One issue stream of NS + NV MFMA slots: slots 0..NS-1 form the next tile's scores, the rest
+    // the value product.  Probability pair q (elements 2q, 2q+1) is computed in slot
+    // (q * SPAN) / 16, spreading the exponentials over the first SPAN slots while every block pb[k]
+    // is complete before the value MFMAs that read it.  Operand fragments come from one LDS ring,
+    // read PF slots ahead.
+    constexpr int NSLOT = NS + NV, SPAN = NS + NV / 2;
+    bf16x8_t fr[PF + 1];
+    auto frag = [&](int j) {
+      return j < NS ? *reinterpret_cast<const bf16x8_t*>(kslot + (j & 1) * 32 * KROW + kaddr[j >> 1])
+                    : *reinterpret_cast<const bf16x8_t*>(vslot + ((j - NS) % DT) * 32 * VROW + vaddr[(j - NS) / DT]);
+    };
 #pragma unroll
-    for (int f = 0; f < PF; ++f) kf[f] = kfrag(f);
+    for (int j = 0; j < PF; ++j) fr[j] = frag(j);
 #pragma unroll
-    for (int f = 0; f < NS; ++f) {
-      if (f + PF < NS) kf[(f + PF) % (PF + 1)] = kfrag(f + PF);
-      else vf[f + PF - NS] = vfrag(f + PF - NS);
-      sn[f & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[f % (PF + 1)], qf[f >> 1], sn[f & 1], 0, 0, 0);
+    for (int j = 0; j < NSLOT; ++j) {
+      if (j + PF < NSLOT) fr[(j + PF) % (PF + 1)] = frag(j + PF);
+      if (j < NS) {
+        sn[j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % (PF + 1)], qf[j >> 1], sn[j & 1], 0, 0, 0);
+      } else {
+        const int f = j - NS;
+        o[f % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[j % (PF + 1)], pb[f / DT], o[f % DT], 0, 0, 0);
+      }
 #pragma unroll
-      for (int x = 0; x < EPC; x += 2) {
-        const int e = f * EPC + x, t = e >> 4, r = e & 15;
+      for (int q = 0; q < 16; ++q) {
+        if ((q * SPAN) / 16 != j) continue;
+        const int e = 2 * q, t = e >> 4, r = e & 15;
         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[t][r], sl2, -mb2));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][r + 1], sl2, -mb2));
         const bf16x2_t pp = {(__bf16)p0, (__bf16)p1};
@@ -251,12 +264,6 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         pb[2 * t + (r >> 3)][(r & 7) + 1] = pp[1];
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int f = 0; f < NV; ++f) {
-      if (f + PF < NV) vf[(f + PF) % (PF + 1)] = vfrag(f + PF);
-      o[f % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[f % (PF + 1)], pb[f / DT], o[f % DT], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     TSA_WAIT_VMEM();
