@@ -52,14 +52,19 @@ def head_scores(Q, K, q):
 
     Q: [L][Hq][d], K: [L][Hkv][d] float64.  Returns s_h: [Hq][L] float64.
     """
-    L, Hq, d = Q.shape
-    Hkv = K.shape[1]
+    return head_scores_recent(Q[Q.shape[0] - q:], K)
+
+
+def head_scores_recent(Q_recent, K):
+    """head_scores given only the recent query rows Q_recent = Q[L-q:] ([q][Hq][d])."""
+    q, Hq, d = Q_recent.shape
+    L, Hkv = K.shape[0], K.shape[1]
     s_h = np.zeros((Hq, L))
     pos = np.arange(L)
     recent = np.arange(L - q, L)                      # query positions p = L-q .. L-1
     for h in range(Hq):
         g = gqa_group(h, Hq, Hkv)
-        z = (Q[recent, h, :] @ K[:, g, :].T) / np.sqrt(d)        # [q][L] logits
+        z = (Q_recent[:, h, :] @ K[:, g, :].T) / np.sqrt(d)      # [q][L] logits
         visible = pos[None, :] <= recent[:, None]                # causal
         z = np.where(visible, z, -np.inf)
         m = z.max(axis=1, keepdims=True)
