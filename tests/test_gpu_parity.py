@@ -1,7 +1,7 @@
 """HIP path vs the CPU oracle, stage by stage and end to end, through the C ABI.
 
 Acceptance rules (restated from the method's parity bar):
-  score      : s_h, s_l within 2e-7 relative (the HIP scores are float64 sums stored as float32)
+  score      : s_h, s_l within 1e-6 relative for bf16 (matrix-core logits), 2e-7 for fp32
   budget     : k exact on the HIP's own float32 s_l (exact rational check), and against the oracle
                either equal or inside the band C(k) >= tau(1-1e-5), C(k-1) < tau(1+1e-5)
   select     : exact top-L' (score desc, index asc) of the HIP's own s_h; against the oracle only
@@ -129,11 +129,19 @@ def assert_close(got, want, dtype, what):
 
 # -- stage 1 --------------------------------------------------------------------------------------
 
+# bf16 logits come from the matrix cores (exact bf16 products, float32 accumulation); everything
+# after the logits is float64.  1e-6 relative keeps any reordering inside the selection's tie band.
+SCORE_RTOL = {"bf16": 1e-6, "f32": 2e-7}
+
+
 def test_score(case):
     s_h, s_l = case.gpu_scores()
     r = case.ref
-    np.testing.assert_allclose(f64(s_h), r["s_h"], rtol=2e-7, atol=1e-30)
-    np.testing.assert_allclose(f64(s_l), r["s_l"], rtol=2e-7, atol=1e-30)
+    rtol = SCORE_RTOL[case.cfg.dtype]
+    np.testing.assert_allclose(f64(s_h), r["s_h"], rtol=rtol, atol=1e-30)
+    np.testing.assert_allclose(f64(s_l), r["s_l"], rtol=rtol, atol=1e-30)
+    err = np.abs(f64(s_h) - r["s_h"]) / r["s_h"]
+    print(f"\n[{case.cfg.name}] s_h relative error: max {err.max():.2e}, median {np.median(err):.2e}")
 
 
 # -- stage 2 --------------------------------------------------------------------------------------
