@@ -59,7 +59,7 @@ def algorithmic(cfg, Lp, union_rows):
     }
 
 
-def cpu_baseline(cfg, inp, Lp_gpu, budget_s=20.0):
+def cpu_baseline(cfg, inp, Lp_gpu, budget_s=12.0):
     """The CPU oracle (float64, as it stands) on a bounded sample of the same workload, scaled to
     one full layer: scoring, budget and selection run in full; gather + attention run on a sample of
     output rows of a few heads and are scaled by the exact causal pair count; decompress + residual
@@ -78,34 +78,105 @@ def cpu_baseline(cfg, inp, Lp_gpu, budget_s=20.0):
     k, Lp = oracle.budget(s_l, float(np.float32(cfg.tau)))
     idx = oracle.select(s_h, Lp)
     t_sel = time.perf_counter() - t0
-    # attention on sampled rows of sampled heads; pair count of row i is i + 1
+    # attention on sampled rows of sampled heads, batches of rows until about budget_s of work;
+    # the pair count of compressed row i is i + 1
     rng = np.random.default_rng(0)
-    heads = [0, cfg.Hq // 2]
-    rows = np.sort(rng.choice(Lp, 24, replace=False))
+    heads = [0, cfg.Hq // 2 + 1]
     t0 = time.perf_counter()
-    for h in heads:
-        g = oracle.gqa_group(h, cfg.Hq, cfg.Hkv)
-        qh, kh, vh = Q[idx[h], h, :], K[idx[h], g, :], V[idx[h], g, :]
-        oracle.attention_rows(qh, kh, vh, idx[h], rows)
-        if time.perf_counter() - t0 > budget_s:
-            break
+    sampled_pairs, n_rows = 0.0, 0
+    per_head = {}
+    while time.perf_counter() - t0 < budget_s:
+        for h in heads:
+            if h not in per_head:
+                g = oracle.gqa_group(h, cfg.Hq, cfg.Hkv)
+                per_head[h] = (Q[idx[h], h, :], K[idx[h], g, :], V[idx[h], g, :])
+            rows = np.sort(rng.choice(Lp, 16, replace=False))
+            qh, kh, vh = per_head[h]
+            oracle.attention_rows(qh, kh, vh, idx[h], rows)
+            sampled_pairs += float(np.sum(rows + 1))
+            n_rows += len(rows)
     t_att = time.perf_counter() - t0
-    sampled_pairs = len(heads) * float(np.sum(rows + 1))
     total_pairs = cfg.Hq * Lp * (Lp + 1) / 2.0
     t_att_full = t_att * total_pairs / sampled_pairs
     # decompress + residual on a sample of rows (cost linear in rows)
-    n_rows = 4096
+    n_dec = 4096
     t0 = time.perf_counter()
-    Oh = np.zeros((cfg.Hq, n_rows, cfg.d))
-    oracle.residual(X[:n_rows], oracle.decompress(Oh, np.tile(np.arange(n_rows), (cfg.Hq, 1)), n_rows))
-    t_sc = (time.perf_counter() - t0) * cfg.L / n_rows
+    Oh = np.zeros((cfg.Hq, n_dec, cfg.d))
+    oracle.residual(X[:n_dec], oracle.decompress(Oh, np.tile(np.arange(n_dec), (cfg.Hq, 1)), n_dec))
+    t_sc = (time.perf_counter() - t0) * cfg.L / n_dec
     total_ms = 1e3 * (t_sel + t_att_full + t_sc)
     return {"value": round(total_ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
             "sample": (f"numpy float64 oracle on this workload: scoring, budget and selection in full "
-                       f"({t_sel:.1f} s); gather+attention on {len(rows)} rows x {len(heads)} heads "
+                       f"({t_sel:.1f} s); gather+attention on {n_rows} random rows of {len(heads)} heads "
                        f"({t_att:.1f} s) scaled by causal pair count to {cfg.Hq} heads x L'={Lp}; "
-                       f"decompress+residual on {n_rows} rows scaled to L={cfg.L}"),
+                       f"decompress+residual on {n_dec} rows scaled to L={cfg.L}"),
             "oracle_k": int(k), "oracle_Lp": int(Lp), "gpu_Lp": int(Lp_gpu)}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_L131072_bf16.txt")
+ATTN_SOURCE = os.path.join(ROOT, "token_sparse_attention_amd", "csrc", "attention.hip")
+
+
+def source_hash(path):
+    import hashlib
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the compressed attention from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, each divided by the factor the same counter reads for a plain copy
+    of known size), or None when that summary is missing or the kernel source has changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def traffic_probe(cfg, dev):
+    """A short run for the counter passes: three compressed-attention launches on this workload's
+    shape (L' = L, random bf16) and three copies of a 1 GiB buffer, the calibration of known size."""
+    s = binding.shape_of(cfg)
+    C = binding.capacity(cfg.L)
+    g = torch.Generator(device=dev).manual_seed(0)
+    Qh = torch.randn(cfg.Hq, C, cfg.d, device=dev, generator=g).to(torch.bfloat16)
+    Kh = torch.randn(cfg.Hq, C, cfg.d, device=dev, generator=g).to(torch.bfloat16)
+    Vht = torch.randn(cfg.Hq, cfg.d, C, device=dev, generator=g).to(torch.bfloat16)
+    Oh = torch.empty_like(Qh)
+    lp = torch.tensor([cfg.L], dtype=torch.int32, device=dev)
+    for _ in range(3):
+        binding.attn_causal(s, Qh, Kh, Vht, lp, Oh)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": cfg.name, "copy_bytes": 1 << 30, "attention_launches": 3}), flush=True)
+
+
+def tau_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
+    """The pages' sparsity regime at this workload's shapes: coverage thresholds that prune roughly
+    17% / 54% / 75% of the (nearly uniform) layer score, layer time and speedup over dense."""
+    out = []
+    for tau in (0.15, 0.50, 0.72):
+        s = binding.shape(cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.q, tau, cfg.dtype)
+        ws = binding.workspace(binding.layer_workspace_bytes(s), Q.device)
+        kLp = torch.zeros(2, dtype=torch.int32, device=Q.device)
+        Y = torch.empty_like(X)
+        ms = timed(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws), steps, warmup, stream)
+        k, Lp = kLp.tolist()
+        out.append({"tau": tau, "k": k, "L_keep": Lp, "pruned_frac": round(k / cfg.L, 4), "layer_ms": round(ms, 3),
+                    "speedup_vs_dense": round(dense_ms / ms, 3)})
+        del ws, Y
+    return out
 
 
 def main():
@@ -115,6 +186,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=4, help="workload number (4 = L=128K headline)")
+    ap.add_argument("--no-tau-sweep", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only run the short kernel sequence used for the rocprofv3 counter passes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer runs on one MI355X (no multi-GPU path is built); "
@@ -127,6 +201,9 @@ def main():
     cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     binding.lib()
+    if args.traffic_probe:
+        traffic_probe(cfg, dev)
+        return
     t_gen = time.perf_counter()
     inp = make_layer(cfg)
     t_gen = time.perf_counter() - t_gen
@@ -211,9 +288,11 @@ def main():
         "stages": stages,
         "roofline": {"bound": "mfma", "kernel": "compressed causal attention (bf16)", "achieved": round(att_tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic()},
         "input_gen_s": round(t_gen, 1),
     }
+    if not args.no_tau_sweep:
+        out["supplementary_tau_sweep"] = tau_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, Lp)
     print(json.dumps(out), flush=True)
