@@ -179,6 +179,23 @@ def tau_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
     return out
 
 
+def ratio_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
+    """The ablation's fixed-ratio budget (s = 0.3 and 0.5 of the tokens pruned regardless of the
+    scores) at this workload's shapes: layer time and speedup over dense."""
+    s = binding.shape_of(cfg)
+    ws = binding.workspace(binding.layer_workspace_bytes(s), Q.device)
+    kLp = torch.zeros(2, dtype=torch.int32, device=Q.device)
+    Y = torch.empty_like(X)
+    out = []
+    for sp in (0.3, 0.5):
+        ms = timed(lambda: binding.layer_ratio(s, sp, Q, K, V, X, Y, kLp, ws), steps, warmup, stream)
+        k, Lp = kLp.tolist()
+        out.append({"sparsity": sp, "k": k, "L_keep": Lp, "layer_ms": round(ms, 3),
+                    "speedup_vs_dense": round(dense_ms / ms, 3)})
+    del ws, Y
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -293,6 +310,8 @@ def main():
     }
     if not args.no_tau_sweep:
         out["supplementary_tau_sweep"] = tau_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1, stream)
+        out["supplementary_fixed_ratio"] = ratio_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1,
+                                                       stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, Lp)
     print(json.dumps(out), flush=True)

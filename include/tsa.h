@@ -135,6 +135,20 @@ int tsa_scatter_residual(const tsa_shape* s, const void* Oh, const int32_t* idx,
 int tsa_layer(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X,
               void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream);
 
+/* Fixed-ratio budget, the baseline the coverage budget is measured against in the ablations (notes,
+ * "Ablations": tau = 0.005 against a fixed s = 0.3, tau = 0.010 against s = 0.5; "Key design 2"
+ * describes the fixed keep ratio it replaces).  The pruned count ignores the scores:
+ *   k = round(sparsity * L), halves rounded up, computed exactly from the float32 value;  L' = L - k.
+ * Writes k to k_dev[0] and L' to Lp_dev[0] (device int32; either may be NULL).  sparsity must lie in
+ * [0, 1] (TSA_ERR_ARG otherwise, NaN included); s->tau is not used.  Needs no workspace. */
+int tsa_budget_ratio(const tsa_shape* s, float sparsity, int32_t* k_dev, int32_t* Lp_dev, void* stream);
+
+/* tsa_layer with the fixed-ratio budget in place of the coverage budget: scoring (s_h only), then
+ * L' from tsa_budget_ratio's rule, then selection, compression, attention, decompression and the
+ * residual exactly as in tsa_layer.  Workspace: tsa_layer_workspace_bytes.  s->tau is not used. */
+int tsa_layer_ratio(const tsa_shape* s, float sparsity, const void* Q, const void* K, const void* V,
+                    const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream);
+
 /* Dense causal attention over the full length with the same kernels (the dense layer that the
  * sparse layers replace; notes, "Overall framework"): Y[t][h] = X[t][h] + O[t][h] (X may be NULL;
  * Y may alias X).  The speedup baseline of the layer. */

@@ -30,7 +30,12 @@ R5  GQA: query head h reads KV head floor(h / (Hq / Hkv)); head h is ranked by i
 R6  Compressed attention is causal by ORIGINAL positions (S_h[j] <= S_h[i]) with scale 1/sqrt(d).
 R7  Decompress writes +0.0 into unselected rows; the residual is Y = X + Decompress(O_hat) per head,
     with no output projection.
+R10 Fixed-ratio budget (the ablation baseline): the pruned count k is s*L rounded to the nearest
+    integer, halves rounded up, on the exact value of the stored float32 ratio s; L' = L - k.
 """
+
+from fractions import Fraction
+import math
 
 import numpy as np
 
@@ -94,6 +99,19 @@ def budget(s_l, tau):
     C = np.concatenate([[0.0], np.cumsum(v)])          # C[j] = sum of the j smallest
     hit = np.nonzero(C >= tau)[0]
     k = int(hit[0]) if len(hit) else L
+    return k, L - k
+
+
+def budget_fixed_ratio(L, sparsity):
+    """The ablation's fixed budget: prune the share s of the L tokens, keep L' = (1 - s) L.
+
+    notes, Ablations (dynamic tau = 0.005 against a fixed s = 0.3, tau = 0.010 against s = 0.5) and
+    Key design 2 (a fixed keep ratio cut the same way at every length, the thing the coverage budget
+    replaces).  Reading R10: k = round(s * L), halves up, in exact rational arithmetic on the stored
+    float32 value of s.  Returns (k, L').
+    """
+    s = Fraction(float(np.float32(sparsity)))
+    k = math.floor(s * L + Fraction(1, 2))
     return k, L - k
 
 
@@ -177,12 +195,14 @@ def residual(X, O):
 
 # -- The whole layer and its dense counterpart ----------------------------------------------------
 
-def layer(Q, K, V, X, tau, q):
-    """One Token Sparse Attention prefill layer, stage by stage.  Returns a dict of every stage."""
+def layer(Q, K, V, X, tau, q, sparsity=None):
+    """One Token Sparse Attention prefill layer, stage by stage.  Returns a dict of every stage.
+
+    With sparsity given, the fixed-ratio budget replaces the coverage budget (tau is then unused)."""
     L = Q.shape[0]
     s_h = head_scores(Q, K, q)
     s_l = layer_score(s_h)
-    k, Lp = budget(s_l, tau)
+    k, Lp = budget(s_l, tau) if sparsity is None else budget_fixed_ratio(L, sparsity)
     idx = select(s_h, Lp)
     Qh, Kh, Vh = gather(Q, K, V, idx)
     Oh = compressed_attention(Qh, Kh, Vh, idx)

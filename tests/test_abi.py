@@ -112,6 +112,19 @@ def test_entry_points_validate_before_launch():
     with pytest.raises(binding.TsaError) as e:
         binding.scatter_residual(s, p, None, None, p, None, p, stream=0)    # no inv and no idx
     assert e.value.status == 1
+    for sp in (-0.25, 1.5, float("nan")):                 # fixed ratio outside [0, 1]
+        with pytest.raises(binding.TsaError) as e:
+            binding.budget_ratio(s, sp, p, p, stream=0)
+        assert e.value.status == 1
+        with pytest.raises(binding.TsaError) as e:
+            binding.layer_ratio(s, sp, p, p, p, None, p, stream=0)
+        assert e.value.status == 1
+    with pytest.raises(binding.TsaError) as e:
+        binding.budget_ratio(s, 0.3, mis, p, stream=0)
+    assert e.value.status == 4
+    with pytest.raises(binding.TsaError) as e:           # layer_ratio still needs its workspace
+        binding.layer_ratio(s, 0.3, p, p, p, None, p, stream=0)
+    assert e.value.status == 5
 
 
 def test_select_sparse_layers_rule():

@@ -353,3 +353,56 @@ def test_empty_keep_set_leaves_residual(gpu):
     assert torch.equal(Y, c.d["X"])
     binding.scatter_residual(c.s, Oh, it, iv, c.lp_tensor(0), None, Y)
     assert (Y == 0).all() and not torch.signbit(Y).any()
+
+
+# -- fixed-ratio budget: the ablation baseline ----------------------------------------------------
+
+def test_budget_ratio_exact(gpu):
+    """k and L' bit-exact against the oracle over lengths up to 2^31 - 1 and ratios including the
+    halfway and denormal cases."""
+    Ls = [1, 2, 5, 10, 777, 4096, 131072, 2 ** 23 - 1, 2 ** 23, 2 ** 31 - 1]
+    sps = [0.0, 1.0, 0.5, 0.3, 0.7, 2.0 ** -24, 1e-30, float(np.nextafter(np.float32(0.5), np.float32(0))),
+           *np.random.default_rng(5).random(20).tolist()]
+    out = torch.full((len(Ls) * len(sps), 2), -1, dtype=torch.int32, device=gpu)
+    want = []
+    for i, (L, sp) in enumerate((L, sp) for L in Ls for sp in sps):
+        binding.budget_ratio(binding.shape(L, 1, 1, 64, 1, 0.0, "bf16"), sp, out[i, 0:1], out[i, 1:2])
+        want.append(list(oracle.budget_fixed_ratio(L, sp)))
+    assert out.tolist() == want
+
+
+@pytest.mark.parametrize("sparsity", [0.3, 0.5])
+def test_layer_ratio_end_to_end(case, sparsity):
+    """tsa_layer_ratio: L' from the fixed ratio, selection exact on the HIP's scores and inside the
+    tie band against the oracle's, Y against the oracle layer on those sets."""
+    cfg = case.cfg
+    ws = binding.workspace(binding.layer_workspace_bytes(case.s), case.dev)
+    kl = torch.zeros(2, dtype=torch.int32, device=case.dev)
+    Y = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.layer_ratio(case.s, sparsity, case.d["Q"], case.d["K"], case.d["V"], case.d["X"], Y, kl, ws)
+    k, Lp = kl.tolist()
+    assert (k, Lp) == oracle.budget_fixed_ratio(cfg.L, sparsity)
+    s_h, _ = case.gpu_scores()
+    idx, inv = case.gpu_select(s_h, Lp)
+    check_selection(idx, inv, Lp, f64(s_h))
+    r = case.ref
+    want_sets = oracle.select(r["s_h"], Lp)
+    for h in range(cfg.Hq):
+        diff = np.setxor1d(idx[h, :Lp], want_sets[h])
+        if len(diff):
+            b = np.sort(r["s_h"][h])[::-1][Lp - 1]
+            assert (np.abs(r["s_h"][h][diff] - b) <= 1e-6 * b).all(), (h, diff)
+    idx = idx[:, :Lp].astype(np.int64)
+    oq, ok, ov = oracle.gather(case.h["Q"], case.h["K"], case.h["V"], idx)
+    Oh = oracle.compressed_attention(oq, ok, ov, idx)
+    want = oracle.residual(case.h["X"], oracle.decompress(Oh, idx, cfg.L))
+    assert_close(f64(Y), want, cfg.dtype, "Y (fixed ratio)")
+    got = f64(Y)
+    for h in range(cfg.Hq):
+        un = np.setdiff1d(np.arange(cfg.L), idx[h])
+        assert (got[un, h] == case.h["X"][un, h]).all()
+    if sparsity == 0.5:
+        # deterministic: a second run is bitwise identical
+        Y2 = case.empty(cfg.L, cfg.Hq, cfg.d)
+        binding.layer_ratio(case.s, sparsity, case.d["Q"], case.d["K"], case.d["V"], case.d["X"], Y2, None, ws)
+        assert torch.equal(Y, Y2)

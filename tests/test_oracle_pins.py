@@ -293,6 +293,50 @@ def test_round_to_storage_matches_library_conversion():
     assert oracle.round_to_storage(halfway, "bf16").tolist() == [1.0, 1.0 + 4 * 2.0 ** -8]
 
 
+def test_budget_fixed_ratio_hand_cases():
+    """Reading R10 on values worked out by hand from the exact float32 ratios."""
+    f = oracle.budget_fixed_ratio
+    assert f(4096, 0.0) == (0, 4096) and f(4096, 1.0) == (4096, 0)
+    assert f(4096, 0.5) == (2048, 2048)
+    assert f(5, 0.5) == (3, 2)                        # 2.5 prunes 3: halves round up
+    assert f(10, 0.7) == (7, 3)                       # float32(0.7) = 0.69999998..: 6.9999998 -> 7
+    assert f(10, 0.3) == (3, 7)                       # float32(0.3) = 0.30000001..
+    assert f(4096, 0.3) == (1229, 2867)               # 1228.80005
+    assert f(131072, 0.3) == (39322, 91750)           # 39321.60156
+    assert f(2 ** 23, 2.0 ** -24) == (1, 2 ** 23 - 1)  # exactly 1/2: rounds up
+    assert f(2 ** 23 - 1, 2.0 ** -24) == (0, 2 ** 23 - 1)
+    assert f(1000, 1e-30) == (0, 1000)                # a denormal-range ratio prunes nothing
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_budget_fixed_ratio_is_the_nearest_count(seed):
+    """Brute force: k is the count in [0, L] nearest to s*L (larger one on a tie), L' = L - k, and
+    k is monotone in s."""
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        L = int(rng.integers(1, 3000))
+        sp = float(np.float32(rng.random()))
+        k, Lp = oracle.budget_fixed_ratio(L, sp)
+        x = Fraction(sp) * L
+        best = min(range(L + 1), key=lambda j: (abs(j - x), -j))
+        assert (k, Lp) == (best, L - best), (L, sp)
+    L = 777
+    ks = [oracle.budget_fixed_ratio(L, float(np.float32(v)))[0] for v in np.linspace(0, 1, 301)]
+    assert all(a <= b for a, b in zip(ks, ks[1:])) and ks[0] == 0 and ks[-1] == L
+
+
+def test_fixed_ratio_swaps_only_the_budget():
+    """The fixed-ratio layer with s = k/L of a coverage-budget layer reproduces that layer."""
+    rng = np.random.default_rng(11)
+    L, Hq, Hkv, d, q = 40, 4, 2, 16, 4
+    Q, K, V, X = (rng.standard_normal(sh) for sh in ((L, Hq, d), (L, Hkv, d), (L, Hkv, d), (L, Hq, d)))
+    a = oracle.layer(Q, K, V, X, tau=0.2, q=q)
+    assert 0 < a["k"] < L
+    b = oracle.layer(Q, K, V, X, tau=0.0, q=q, sparsity=a["k"] / L)
+    assert (b["k"], b["Lp"]) == (a["k"], a["Lp"]) and (b["idx"] == a["idx"]).all()
+    assert np.array_equal(b["Y"], a["Y"])
+
+
 def test_sparse_layers_and_drift():
     R = [0.4, 0.3, 0.5, 0.1, 0.2, 0.05, 0.45, 0.35]
     assert oracle.sparse_layers(R) == [2, 4, 5, 6]
@@ -336,7 +380,13 @@ def _mut_attention_no_scale(Qh, Kh, Vh, pos, rows=None):
     return e / e.sum(1, keepdims=True) @ Vh
 
 
+def _mut_ratio_floor(L, sparsity):
+    k = math.floor(Fraction(float(np.float32(sparsity))) * L)
+    return k, L - k
+
+
 @pytest.mark.parametrize("name,mutant,pin", [
+    ("budget_fixed_ratio", _mut_ratio_floor, test_budget_fixed_ratio_hand_cases),
     ("head_scores", _mut_no_causal, lambda: test_score_zero_keys_closed_form(64, 16)),
     ("budget", _mut_budget_strict, lambda: test_budget_exhaustive_exact(0)),
     ("select", _mut_select_high_index_ties, test_select_zero_keys_keeps_the_prefix),

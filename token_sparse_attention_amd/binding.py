@@ -39,6 +39,8 @@ _SIGS = {
     "tsa_scatter_residual": [_P, _P, _P, _P, _P, _P, _P],
     "tsa_layer": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_dense_attn_causal": [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_budget_ratio": [ctypes.c_float, _P, _P, _P],
+    "tsa_layer_ratio": [ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
 EXPORTS = ["tsa_status_string", "tsa_check_args", "tsa_capacity", "tsa_stage_workspace_bytes",
            "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SIGS]
@@ -168,6 +170,17 @@ def layer(s, Q, K, V, X, Y, kLp_dev=None, ws=None, stream=None):
     p, n = _ws(ws)
     _check("tsa_layer", lib().tsa_layer(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y),
                                         _ptr(kLp_dev), p, n, _stream(stream)))
+
+
+def budget_ratio(s, sparsity, k_dev=None, Lp_dev=None, stream=None):
+    _check("tsa_budget_ratio", lib().tsa_budget_ratio(ctypes.byref(s), float(sparsity), _ptr(k_dev),
+                                                      _ptr(Lp_dev), _stream(stream)))
+
+
+def layer_ratio(s, sparsity, Q, K, V, X, Y, kLp_dev=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_layer_ratio", lib().tsa_layer_ratio(ctypes.byref(s), float(sparsity), _ptr(Q), _ptr(K), _ptr(V),
+                                                    _ptr(X), _ptr(Y), _ptr(kLp_dev), p, n, _stream(stream)))
 
 
 def dense_attn_causal(s, Q, K, V, X, Y, ws=None, stream=None):

@@ -110,6 +110,54 @@ uint64_t budget_target(float tau) {
   return (uint64_t)std::ceil(std::ldexp((double)tau, 60));
 }
 
+// Stages 1-5 of the layer on one stream.  fixed_ratio selects the ablation's fixed budget
+// (k = round(sparsity * L)) in place of the coverage budget; s_l is then not needed.
+int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* Q, const void* K,
+              const void* V, const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes,
+              void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Q, K, V, Y}));
+  TSA_TRY(opt_ptrs({X}));
+  if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
+  const LayerWs w = layer_layout(s);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  hipStream_t st = stream_of(stream);
+  const StageWs& g = w.st;
+  const int64_t C = tsa_capacity(s->L);
+  float* s_h = at<float>(ws, w.s_h);
+  float* s_l = at<float>(ws, w.s_l);
+  int32_t* kLp = at<int32_t>(ws, g.kLp);
+  int32_t* idx = at<int32_t>(ws, w.idx);
+  int32_t* inv = at<int32_t>(ws, w.inv);
+  hipError_t e = fixed_ratio ? hipSuccess : launch_fill_zero(at<char>(ws, g.bhist), g.kLp - g.bhist, st);
+  if (e == hipSuccess) e = launch_fill_zero(at<char>(ws, g.shist), g.tcnt - g.shist, st);
+  if (e == hipSuccess)
+    e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h, at<double2>(ws, g.partials),
+                     at<double2>(ws, g.rowstat), st);
+  if (fixed_ratio) {
+    if (e == hipSuccess)
+      e = launch_budget_ratio(sparsity, s->L, kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
+  } else {
+    if (e == hipSuccess)
+      e = launch_layer_score(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l, st);
+    if (e == hipSuccess)
+      e = launch_budget(s_l, s->L, budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl),
+                        kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
+  }
+  if (e == hipSuccess)
+    e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
+                      at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
+  if (e == hipSuccess)
+    e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C, at<void>(ws, w.Qh),
+                      at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
+  if (e == hipSuccess)
+    e = launch_attention(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
+                         kLp + 1, s->L, s->Hq, s->Hkv, C, nullptr, at<void>(ws, w.Oh), st);
+  if (e == hipSuccess)
+    e = launch_scatter(s->dtype, s->d, at<void>(ws, w.Oh), idx, inv, kLp + 1, X, Y, s->L, s->Hq, C, st);
+  return hip_status(e);
+}
+
 }  // namespace
 
 extern "C" {
@@ -233,41 +281,20 @@ int tsa_scatter_residual(const tsa_shape* s, const void* Oh, const int32_t* idx,
 
 int tsa_layer(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X, void* Y,
               int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream) {
+  return run_layer(s, false, 0.f, Q, K, V, X, Y, kLp_dev, ws, ws_bytes, stream);
+}
+
+int tsa_budget_ratio(const tsa_shape* s, float sparsity, int32_t* k_dev, int32_t* Lp_dev, void* stream) {
   TSA_TRY(tsa_check_args(s));
-  TSA_TRY(need_ptrs({Q, K, V, Y}));
-  TSA_TRY(opt_ptrs({X}));
-  if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
-  const LayerWs w = layer_layout(s);
-  TSA_TRY(check_ws(ws, ws_bytes, w.total));
-  hipStream_t st = stream_of(stream);
-  const StageWs& g = w.st;
-  const int64_t C = tsa_capacity(s->L);
-  float* s_h = at<float>(ws, w.s_h);
-  float* s_l = at<float>(ws, w.s_l);
-  int32_t* kLp = at<int32_t>(ws, g.kLp);
-  int32_t* idx = at<int32_t>(ws, w.idx);
-  int32_t* inv = at<int32_t>(ws, w.inv);
-  hipError_t e = launch_fill_zero(at<char>(ws, g.bhist), g.kLp - g.bhist, st);
-  if (e == hipSuccess) e = launch_fill_zero(at<char>(ws, g.shist), g.tcnt - g.shist, st);
-  if (e == hipSuccess)
-    e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h, at<double2>(ws, g.partials),
-                     at<double2>(ws, g.rowstat), st);
-  if (e == hipSuccess) e = launch_layer_score(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l, st);
-  if (e == hipSuccess)
-    e = launch_budget(s_l, s->L, budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl), kLp,
-                      kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
-  if (e == hipSuccess)
-    e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
-                      at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
-  if (e == hipSuccess)
-    e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C, at<void>(ws, w.Qh),
-                      at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
-  if (e == hipSuccess)
-    e = launch_attention(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
-                         kLp + 1, s->L, s->Hq, s->Hkv, C, nullptr, at<void>(ws, w.Oh), st);
-  if (e == hipSuccess)
-    e = launch_scatter(s->dtype, s->d, at<void>(ws, w.Oh), idx, inv, kLp + 1, X, Y, s->L, s->Hq, C, st);
-  return hip_status(e);
+  if (!(sparsity >= 0.f && sparsity <= 1.f)) return TSA_ERR_ARG;   // also rejects NaN
+  if ((k_dev && ((uintptr_t)k_dev & 3u)) || (Lp_dev && ((uintptr_t)Lp_dev & 3u))) return TSA_ERR_ALIGN;
+  return hip_status(launch_budget_ratio(sparsity, s->L, nullptr, k_dev, Lp_dev, stream_of(stream)));
+}
+
+int tsa_layer_ratio(const tsa_shape* s, float sparsity, const void* Q, const void* K, const void* V,
+                    const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!(sparsity >= 0.f && sparsity <= 1.f)) return TSA_ERR_ARG;
+  return run_layer(s, true, sparsity, Q, K, V, X, Y, kLp_dev, ws, ws_bytes, stream);
 }
 
 int tsa_dense_attn_causal(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X,

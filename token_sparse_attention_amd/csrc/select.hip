@@ -227,6 +227,29 @@ hipError_t launch_budget(const float* s_l, int64_t L, uint64_t target, uint64_t*
   return hipGetLastError();
 }
 
+// Fixed-ratio budget: k = round(s * L), halves up, exact on the float32 value of s (s in [0, 1]).
+// s = M * 2^-sh with an integer mantissa M < 2^24 and sh >= 23, so M * L < 2^55 and
+// k = (M * L + 2^(sh-1)) >> sh fits 64-bit arithmetic; for sh >= 64, s * L < 1/2 and k = 0.
+__global__ void budget_ratio_kernel(float s, int64_t L, int32_t* __restrict__ kLp_ws,
+                                    int32_t* __restrict__ k_out, int32_t* __restrict__ Lp_out) {
+  if (threadIdx.x != 0) return;
+  const uint32_t bits = __float_as_uint(s);
+  const uint32_t e = (bits >> 23) & 255u;
+  const uint64_t M = e ? (uint64_t)((bits & 0x7FFFFFu) | 0x800000u) : (uint64_t)(bits & 0x7FFFFFu);
+  const int sh = e ? 150 - (int)e : 149;
+  int64_t k = 0;
+  if (sh < 64) k = (int64_t)((M * (uint64_t)L + (1ull << (sh - 1))) >> sh);
+  if (kLp_ws) { kLp_ws[0] = (int32_t)k; kLp_ws[1] = (int32_t)(L - k); }
+  if (k_out) k_out[0] = (int32_t)k;
+  if (Lp_out) Lp_out[0] = (int32_t)(L - k);
+}
+
+hipError_t launch_budget_ratio(float sparsity, int64_t L, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
+                               hipStream_t st) {
+  budget_ratio_kernel<<<1, 64, 0, st>>>(sparsity, L, kLp_ws, k_out, Lp_out);
+  return hipGetLastError();
+}
+
 // ---- per-head selection -------------------------------------------------------------------------
 
 struct SelThr {

@@ -36,6 +36,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_budget(const float* s_l, int64_t L, uint64_t target, uint64_t* hist,
                          RadixCtl* ctl, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
                          hipStream_t st);
+// Fixed-ratio budget: k = round(sparsity * L) (halves up); writes like launch_budget (kLp_ws may be null).
+hipError_t launch_budget_ratio(float sparsity, int64_t L, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
+                               hipStream_t st);
 int64_t select_tiles(int64_t L);
 hipError_t launch_select(const float* s_h, int64_t L, int Hq, const int32_t* Lp_dev,
                          uint64_t* hist, RadixCtl* ctl, uint32_t* tile_cnt, uint32_t* tile_off,
