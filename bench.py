@@ -22,7 +22,7 @@ sys.path.insert(0, ROOT)
 
 from token_sparse_attention_amd import binding  # noqa: E402
 from token_sparse_attention_amd.configs import CONFIGS  # noqa: E402
-from token_sparse_attention_amd.inputs import make_layer  # noqa: E402
+from token_sparse_attention_amd.inputs import make_batch, make_layer  # noqa: E402
 
 METRIC = "TSA layer ms & speedup vs own dense attn at L=128K; MFMA util, HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -196,6 +196,50 @@ def ratio_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
     return out
 
 
+VARLEN_LENGTHS = [32768, 24576, 16384, 16384, 8192, 8192, 4096, 4096]
+
+
+def varlen_batch(steps, warmup, stream, dev):
+    """A ragged batch (8 samples of 4K-32K tokens, the 32K workload's recipe, one independent draw
+    per sample): the batched layer with one attention launch over every sample's keep count, the
+    same samples one tsa_layer call after another, and the batched dense baseline."""
+    cfg = CONFIGS[3]
+    b = make_batch(cfg, VARLEN_LENGTHS)
+    cu = [int(v) for v in b["cu_seqlens"]]
+    Q, K, V, X = (b[n].to(dev) for n in ("Q", "K", "V", "X"))
+    out = {"workload": f"varlen batch of {len(cu) - 1} ({cfg.name} recipe)", "lengths": VARLEN_LENGTHS,
+           "tokens": cu[-1]}
+    for tau in (cfg.tau, 0.5):
+        s = binding.shape(cu[-1], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, tau, cfg.dtype)
+        ws = binding.workspace(binding.layer_varlen_workspace_bytes(s, cu), dev)
+        kLp = torch.zeros(len(cu) - 1, 2, dtype=torch.int32, device=dev)
+        Y = torch.empty_like(X)
+        ms = timed(lambda: binding.layer_varlen(s, cu, Q, K, V, X, Y, kLp, ws), steps, warmup, stream)
+        del ws
+        per = []
+        for i in range(len(cu) - 1):
+            sb = binding.shape(cu[i + 1] - cu[i], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, tau, cfg.dtype)
+            r = slice(cu[i], cu[i + 1])
+            per.append((sb, Q[r], K[r], V[r], X[r], Y[r], binding.workspace(binding.layer_workspace_bytes(sb), dev)))
+
+        def one_by_one():
+            for sb, q_, k_, v_, x_, y_, w_ in per:
+                binding.layer(sb, q_, k_, v_, x_, y_, None, w_)
+        ms_seq = timed(one_by_one, steps, warmup, stream)
+        del per
+        out[f"tau_{tau}"] = {"keep_counts": [int(v) for v in kLp[:, 1].tolist()], "layer_varlen_ms": round(ms, 3),
+                             "per_sample_layers_ms": round(ms_seq, 3),
+                             "tokens_per_s": round(cu[-1] / (ms * 1e-3), 1)}
+    s = binding.shape(cu[-1], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, cfg.tau, cfg.dtype)
+    dws = binding.workspace(binding.dense_varlen_workspace_bytes(s, cu), dev)
+    Yd = torch.empty_like(X)
+    dms = timed(lambda: binding.dense_attn_causal_varlen(s, cu, Q, K, V, X, Yd, dws), steps, warmup, stream)
+    out["dense_varlen_ms"] = round(dms, 3)
+    for tau in (cfg.tau, 0.5):
+        out[f"tau_{tau}"]["speedup_vs_dense"] = round(dms / out[f"tau_{tau}"]["layer_varlen_ms"], 3)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +248,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", type=int, default=4, help="workload number (4 = L=128K headline)")
     ap.add_argument("--no-tau-sweep", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the short kernel sequence used for the rocprofv3 counter passes")
     args = ap.parse_args()
@@ -312,6 +357,9 @@ def main():
         out["supplementary_tau_sweep"] = tau_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1, stream)
         out["supplementary_fixed_ratio"] = ratio_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1,
                                                        stream)
+    if not args.no_varlen:
+        del Qh, Kh, Vht, Oh, Ys, ws, sws
+        out["supplementary_varlen"] = varlen_batch(max(2, args.steps // 2), 1, stream, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, Lp)
     print(json.dumps(out), flush=True)

@@ -155,6 +155,44 @@ int tsa_layer_ratio(const tsa_shape* s, float sparsity, const void* Q, const voi
 int tsa_dense_attn_causal(const tsa_shape* s, const void* Q, const void* K, const void* V,
                           const void* X, void* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Batches of sequences of different lengths (varlen) -------------------------------------
+ * The keep count L' is data dependent, so the samples of a batch compress to different lengths
+ * (notes, "Limitations", names this raggedness as a practical cost of batching).  A batch packs B
+ * independent sequences along the token dimension: sample b owns tokens [cu[b], cu[b+1]) of Q, K,
+ * V, X and Y, where cu_seqlens is a HOST array of B+1 int64 with cu[0] = 0, cu[b] < cu[b+1] and
+ * cu[B] = s->L (the total).  Every sample shares Hq, Hkv, d, q, tau and dtype, and needs
+ * cu[b+1] - cu[b] >= q (TSA_ERR_SHAPE otherwise; a malformed cu gives TSA_ERR_ARG).  Each sample
+ * gets its own scores, budget, keep count L'_b and selection, exactly as tsa_layer on that sample
+ * alone.
+ * Compressed tensors of a batch: sample b's region has the one-sequence layout for its length L_b
+ * (Qh, Kh, Oh [Hq][C_b][d], Vht [Hq][d][C_b], C_b = tsa_capacity(L_b)) and starts at element
+ * Hq*d*P_b, with P_b = C_0 + ... + C_{b-1}; the total row capacity is tsa_varlen_capacity(). */
+
+/* P_B = sum of the per-sample capacities, or -1 if cu_seqlens is malformed.  Host only. */
+int64_t tsa_varlen_capacity(int32_t B, const int64_t* cu_seqlens);
+/* Workspace of tsa_layer_varlen / tsa_dense_attn_causal_varlen (0 for invalid arguments). */
+size_t tsa_layer_varlen_workspace_bytes(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens);
+size_t tsa_dense_varlen_workspace_bytes(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens);
+
+/* Stage 4b over a batch in ONE launch: tsa_attn_causal for every sample, sample b reading its
+ * keep count from Lp_dev[b] (device int32[B]).  Longer samples are scheduled first. */
+int tsa_attn_causal_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, const void* Qh,
+                           const void* Kh, const void* Vht, const int32_t* Lp_dev, void* Oh, void* stream);
+
+/* tsa_layer for every sample of the batch.  Scoring, budget, selection, compression and
+ * decompression run sample after sample on `stream` (each is O(L_b)); the attention runs as one
+ * launch over all samples' ragged keep counts.  kLp_dev (optional) receives {k_b, L'_b} per sample
+ * (device int32[B][2]).  Y may alias X.  Workspace: tsa_layer_varlen_workspace_bytes. */
+int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, const void* Q, const void* K,
+                     const void* V, const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/* tsa_dense_attn_causal for every sample of the batch, the attention in one launch (the dense
+ * baseline of tsa_layer_varlen).  Workspace: tsa_dense_varlen_workspace_bytes. */
+int tsa_dense_attn_causal_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, const void* Q,
+                                 const void* K, const void* V, const void* X, void* Y, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -211,6 +211,20 @@ def layer(Q, K, V, X, tau, q, sparsity=None):
     return dict(s_h=s_h, s_l=s_l, k=k, Lp=Lp, idx=idx, Qh=Qh, Kh=Kh, Vh=Vh, Oh=Oh, O=O, Y=Y)
 
 
+def layer_varlen(Q, K, V, X, cu_seqlens, tau, q):
+    """A batch of independent sequences packed along the token axis (sample b owns tokens
+    cu_seqlens[b] .. cu_seqlens[b+1]-1): each sample is one layer on its own, with its own scores,
+    budget and keep count, so the keep counts differ across the batch (notes, Limitations: the
+    ragged L' of batched inference).  Returns the per-sample stage dicts and the packed Y."""
+    outs, Ys = [], []
+    for b in range(len(cu_seqlens) - 1):
+        t = slice(cu_seqlens[b], cu_seqlens[b + 1])
+        r = layer(Q[t], K[t], V[t], None if X is None else X[t], tau, q)
+        outs.append(r)
+        Ys.append(r["Y"])
+    return outs, np.concatenate(Ys, axis=0)
+
+
 def dense_attention_rows(Q, K, V, h, rows=None):
     """Full-length causal attention of query head h with its GQA KV head (the dense baseline that
     the sparse layers replace; notes, Overall framework: non-sparse layers keep dense attention)."""

@@ -143,3 +143,28 @@ def test_every_kernel_has_its_host_launch_stub():
     out = subprocess.run(["nm", "-D", "--undefined-only", binding._LIB_PATH], capture_output=True, text=True)
     assert out.returncode == 0, out.stderr
     assert "__device_stub__" not in out.stdout
+
+
+def test_varlen_capacity_and_validation():
+    """Host-side rules of the varlen batch entry points (nothing is launched on these paths)."""
+    assert binding.varlen_capacity([0, 1, 300, 1000]) == 256 + 512 + 768
+    assert binding.varlen_capacity([0, 4096]) == 4096
+    assert binding.varlen_capacity([0, 5, 5]) == -1 and binding.varlen_capacity([1, 5]) == -1
+    s = binding.shape(1000, 4, 2, 128, 5, 0.05, "bf16")
+    cu = [0, 37, 700, 1000]
+    assert binding.layer_varlen_workspace_bytes(s, cu) >= 4 * 128 * 2 * 4 * binding.varlen_capacity(cu)
+    assert binding.dense_varlen_workspace_bytes(s, cu) >= 2 * 128 * 2 * binding.varlen_capacity(cu)
+    for bad, status in (([0, 37, 700, 999], 1), ([0, 700, 37, 1000], 1), ([1, 37, 700, 1000], 1),
+                        ([0, 3, 700, 1000], 2)):              # last: a sample shorter than q = 5
+        assert binding.layer_varlen_workspace_bytes(s, bad) == 0
+        p = FakePtr(1 << 20)
+        with pytest.raises(binding.TsaError) as e:
+            binding.layer_varlen(s, bad, p, p, p, None, p, stream=0)
+        assert e.value.status == status, bad
+        with pytest.raises(binding.TsaError) as e:
+            binding.attn_causal_varlen(s, bad, p, p, p, p, p, stream=0)
+        assert e.value.status == status, bad
+    p = FakePtr(1 << 20)
+    with pytest.raises(binding.TsaError) as e:                # valid batch, no workspace
+        binding.layer_varlen(s, cu, p, p, p, None, p, stream=0)
+    assert e.value.status == 5

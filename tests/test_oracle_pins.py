@@ -337,6 +337,29 @@ def test_fixed_ratio_swaps_only_the_budget():
     assert np.array_equal(b["Y"], a["Y"])
 
 
+def test_varlen_batch_keeps_samples_apart():
+    """Samples of a batch never see each other: the first token of every sample attends to itself
+    only (its output is its own value row, plus the residual), changing one sample leaves the
+    others bit-identical, and identical samples give identical outputs."""
+    rng = np.random.default_rng(21)
+    lens = [30, 1, 17, 30]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, Hq, Hkv, d, q = cu[-1], 4, 2, 16, 1
+    Q, K, V, X = (rng.standard_normal(sh) for sh in ((T, Hq, d), (T, Hkv, d), (T, Hkv, d), (T, Hq, d)))
+    # sample 3 repeats sample 0
+    Q[cu[3]:], K[cu[3]:], V[cu[3]:], X[cu[3]:] = Q[:30], K[:30], V[:30], X[:30]
+    outs, Y = oracle.layer_varlen(Q, K, V, X, cu, tau=0.0, q=q)
+    assert [o["Lp"] for o in outs] == lens                # tau = 0 keeps everything
+    for b in range(4):
+        assert np.allclose(Y[cu[b]], X[cu[b]] + V[cu[b]][np.arange(Hq) // (Hq // Hkv)], rtol=0, atol=1e-15)
+    assert np.array_equal(Y[cu[3]:], Y[:30])
+    K2 = K.copy()
+    K2[cu[2]:cu[3]] += 1.0
+    _, Y2 = oracle.layer_varlen(Q, K2, V, X, cu, tau=0.0, q=q)
+    keep = np.r_[0:cu[2], cu[3]:T]
+    assert np.array_equal(Y2[keep], Y[keep]) and not np.array_equal(Y2[cu[2]:cu[3]], Y[cu[2]:cu[3]])
+
+
 def test_sparse_layers_and_drift():
     R = [0.4, 0.3, 0.5, 0.1, 0.2, 0.05, 0.45, 0.35]
     assert oracle.sparse_layers(R) == [2, 4, 5, 6]

@@ -41,9 +41,13 @@ _SIGS = {
     "tsa_dense_attn_causal": [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_budget_ratio": [ctypes.c_float, _P, _P, _P],
     "tsa_layer_ratio": [ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_attn_causal_varlen": [ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_layer_varlen": [ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_dense_attn_causal_varlen": [ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
+_VARLEN_WS = ("tsa_layer_varlen_workspace_bytes", "tsa_dense_varlen_workspace_bytes")
 EXPORTS = ["tsa_status_string", "tsa_check_args", "tsa_capacity", "tsa_stage_workspace_bytes",
-           "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SIGS]
+           "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SIGS, "tsa_varlen_capacity", *_VARLEN_WS]
 
 
 def lib():
@@ -67,6 +71,11 @@ def lib():
         for n, args in _SIGS.items():
             getattr(L, n).restype = ctypes.c_int
             getattr(L, n).argtypes = [sp, *args]
+        L.tsa_varlen_capacity.restype = ctypes.c_int64
+        L.tsa_varlen_capacity.argtypes = [ctypes.c_int32, _P]
+        for n in _VARLEN_WS:
+            getattr(L, n).restype = ctypes.c_size_t
+            getattr(L, n).argtypes = [sp, ctypes.c_int32, _P]
         _lib = L
     return _lib
 
@@ -187,3 +196,48 @@ def dense_attn_causal(s, Q, K, V, X, Y, ws=None, stream=None):
     p, n = _ws(ws)
     _check("tsa_dense_attn_causal", lib().tsa_dense_attn_causal(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
                                                                 _ptr(X), _ptr(Y), p, n, _stream(stream)))
+
+
+# -- varlen batches: cu_seqlens is a host sequence of B+1 token offsets ---------------------------
+
+def _cu(cu_seqlens):
+    arr = (ctypes.c_int64 * len(cu_seqlens))(*[int(v) for v in cu_seqlens])
+    return ctypes.c_int32(len(cu_seqlens) - 1), arr
+
+
+def varlen_capacity(cu_seqlens):
+    B, arr = _cu(cu_seqlens)
+    return lib().tsa_varlen_capacity(B, ctypes.cast(arr, _P))
+
+
+def layer_varlen_workspace_bytes(s, cu_seqlens):
+    B, arr = _cu(cu_seqlens)
+    return lib().tsa_layer_varlen_workspace_bytes(ctypes.byref(s), B, ctypes.cast(arr, _P))
+
+
+def dense_varlen_workspace_bytes(s, cu_seqlens):
+    B, arr = _cu(cu_seqlens)
+    return lib().tsa_dense_varlen_workspace_bytes(ctypes.byref(s), B, ctypes.cast(arr, _P))
+
+
+def attn_causal_varlen(s, cu_seqlens, Qh, Kh, Vht, Lp_dev, Oh, stream=None):
+    B, arr = _cu(cu_seqlens)
+    _check("tsa_attn_causal_varlen", lib().tsa_attn_causal_varlen(
+        ctypes.byref(s), B, ctypes.cast(arr, _P), _ptr(Qh), _ptr(Kh), _ptr(Vht), _ptr(Lp_dev), _ptr(Oh),
+        _stream(stream)))
+
+
+def layer_varlen(s, cu_seqlens, Q, K, V, X, Y, kLp_dev=None, ws=None, stream=None):
+    B, arr = _cu(cu_seqlens)
+    p, n = _ws(ws)
+    _check("tsa_layer_varlen", lib().tsa_layer_varlen(
+        ctypes.byref(s), B, ctypes.cast(arr, _P), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y), _ptr(kLp_dev), p, n,
+        _stream(stream)))
+
+
+def dense_attn_causal_varlen(s, cu_seqlens, Q, K, V, X, Y, ws=None, stream=None):
+    B, arr = _cu(cu_seqlens)
+    p, n = _ws(ws)
+    _check("tsa_dense_attn_causal_varlen", lib().tsa_dense_attn_causal_varlen(
+        ctypes.byref(s), B, ctypes.cast(arr, _P), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y), p, n,
+        _stream(stream)))

@@ -2,8 +2,10 @@
 // the stage-by-stage orchestration of the Token Sparse Attention prefill layer.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "tsa.h"
 #include "tsa_internal.h"
@@ -108,6 +110,77 @@ int need_int_ptrs(std::initializer_list<const void*> ps) {
 uint64_t budget_target(float tau) {
   // ceil(tau * 2^60): the integer fixed-point mass that "C(j) >= tau" must reach.
   return (uint64_t)std::ceil(std::ldexp((double)tau, 60));
+}
+
+// ---- varlen batches ------------------------------------------------------------------------------
+
+int check_varlen(const tsa_shape* s, int32_t B, const int64_t* cu) {
+  TSA_TRY(tsa_check_args(s));
+  if (B < 1 || cu == nullptr || cu[0] != 0 || cu[B] != s->L) return TSA_ERR_ARG;
+  for (int32_t b = 0; b < B; ++b) {
+    if (cu[b + 1] <= cu[b]) return TSA_ERR_ARG;
+    if (cu[b + 1] - cu[b] < s->q) return TSA_ERR_SHAPE;
+  }
+  return TSA_OK;
+}
+
+// One sequence of the batch viewed as a single-sequence problem.
+tsa_shape sample_shape(const tsa_shape* s, const int64_t* cu, int32_t b) {
+  tsa_shape t = *s;
+  t.L = cu[b + 1] - cu[b];
+  return t;
+}
+
+int64_t max_len(int32_t B, const int64_t* cu) {
+  int64_t m = 0;
+  for (int32_t b = 0; b < B; ++b) m = std::max(m, cu[b + 1] - cu[b]);
+  return m;
+}
+
+int64_t varlen_capacity(int32_t B, const int64_t* cu) {
+  int64_t P = 0;
+  for (int32_t b = 0; b < B; ++b) P += tsa_capacity(cu[b + 1] - cu[b]);
+  return P;
+}
+
+// Sequences in launch order: longest first (they hold the heaviest query blocks).
+std::vector<int32_t> longest_first(int32_t B, const int64_t* cu) {
+  std::vector<int32_t> order(B);
+  for (int32_t b = 0; b < B; ++b) order[b] = b;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return cu[x + 1] - cu[x] > cu[y + 1] - cu[y]; });
+  return order;
+}
+
+// Workspace of tsa_layer_varlen: one stage workspace for the longest sample (reused sample after
+// sample on the stream) + per-sample {k, L'} pairs + the batch's intermediates.
+struct VarlenWs {
+  StageWs st;
+  size_t kLp, s_h, s_l, idx, inv, Qh, Kh, Vht, Oh, total;
+};
+
+VarlenWs varlen_layout(const tsa_shape* s, int32_t B, const int64_t* cu) {
+  VarlenWs w;
+  tsa_shape big = *s;
+  big.L = max_len(B, cu);
+  w.st = stage_layout(&big);
+  size_t o = w.st.total;
+  auto take = [&](size_t n) { size_t at = o; o += up(n); return at; };
+  // per-sample regions of the score and index arrays start at the capacity offsets P_b (multiples
+  // of 256 rows) like the compressed tensors, so every region is aligned whatever the lengths
+  const size_t P = (size_t)varlen_capacity(B, cu);
+  const size_t comp = (size_t)s->Hq * P * s->d * elem_bytes(s->dtype);
+  w.kLp = take((size_t)B * 2 * sizeof(int32_t));
+  w.s_h = take((size_t)s->Hq * P * sizeof(float));
+  w.s_l = take(P * sizeof(float));
+  w.idx = take((size_t)s->Hq * P * sizeof(int32_t));
+  w.inv = take((size_t)s->Hq * P * sizeof(int32_t));
+  w.Qh = take(comp);
+  w.Kh = take(comp);
+  w.Vht = take(comp);
+  w.Oh = take(comp);
+  w.total = o;
+  return w;
 }
 
 // Stages 1-5 of the layer on one stream.  fixed_ratio selects the ablation's fixed budget
@@ -308,6 +381,124 @@ int tsa_dense_attn_causal(const tsa_shape* s, const void* Q, const void* K, cons
   hipError_t e = launch_transpose_v(s->dtype, s->d, V, s->L, s->Hkv, C, ws, st);
   if (e == hipSuccess)
     e = launch_attention(s->dtype, s->d, true, Q, K, ws, nullptr, s->L, s->Hq, s->Hkv, C, X, Y, st);
+  return hip_status(e);
+}
+
+int64_t tsa_varlen_capacity(int32_t B, const int64_t* cu_seqlens) {
+  if (B < 1 || cu_seqlens == nullptr || cu_seqlens[0] != 0) return -1;
+  for (int32_t b = 0; b < B; ++b)
+    if (cu_seqlens[b + 1] <= cu_seqlens[b]) return -1;
+  return varlen_capacity(B, cu_seqlens);
+}
+
+size_t tsa_layer_varlen_workspace_bytes(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens) {
+  return check_varlen(s, B, cu_seqlens) == TSA_OK ? varlen_layout(s, B, cu_seqlens).total : 0;
+}
+
+size_t tsa_dense_varlen_workspace_bytes(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens) {
+  if (check_varlen(s, B, cu_seqlens) != TSA_OK) return 0;
+  return up((size_t)s->Hkv * s->d * varlen_capacity(B, cu_seqlens) * elem_bytes(s->dtype));
+}
+
+int tsa_attn_causal_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, const void* Qh,
+                           const void* Kh, const void* Vht, const int32_t* Lp_dev, void* Oh, void* stream) {
+  TSA_TRY(check_varlen(s, B, cu_seqlens));
+  TSA_TRY(need_ptrs({Qh, Kh, Vht, Oh}));
+  TSA_TRY(need_int_ptrs({Lp_dev}));
+  std::vector<AttnSeqDesc> seqs;
+  std::vector<int64_t> P(B + 1, 0);
+  for (int32_t b = 0; b < B; ++b) P[b + 1] = P[b] + tsa_capacity(cu_seqlens[b + 1] - cu_seqlens[b]);
+  for (int32_t b : longest_first(B, cu_seqlens))
+    seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], Lp_dev + b});
+  return hip_status(launch_attention_varlen(s->dtype, s->d, false, Qh, Kh, Vht, B, seqs.data(), s->Hq, s->Hkv,
+                                            nullptr, Oh, stream_of(stream)));
+}
+
+int tsa_dense_attn_causal_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, const void* Q,
+                                 const void* K, const void* V, const void* X, void* Y, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  TSA_TRY(check_varlen(s, B, cu_seqlens));
+  TSA_TRY(need_ptrs({Q, K, V, Y}));
+  TSA_TRY(opt_ptrs({X}));
+  TSA_TRY(check_ws(ws, ws_bytes, tsa_dense_varlen_workspace_bytes(s, B, cu_seqlens)));
+  hipStream_t st = stream_of(stream);
+  const size_t eb = elem_bytes(s->dtype);
+  std::vector<AttnSeqDesc> seqs;
+  std::vector<int64_t> P(B + 1, 0);
+  for (int32_t b = 0; b < B; ++b) P[b + 1] = P[b] + tsa_capacity(cu_seqlens[b + 1] - cu_seqlens[b]);
+  hipError_t e = hipSuccess;
+  for (int32_t b = 0; b < B && e == hipSuccess; ++b) {
+    const int64_t Lb = cu_seqlens[b + 1] - cu_seqlens[b];
+    e = launch_transpose_v(s->dtype, s->d, static_cast<const char*>(V) + (size_t)cu_seqlens[b] * s->Hkv * s->d * eb,
+                           Lb, s->Hkv, P[b + 1] - P[b], static_cast<char*>(ws) + (size_t)P[b] * s->Hkv * s->d * eb, st);
+  }
+  for (int32_t b : longest_first(B, cu_seqlens))
+    seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], nullptr});
+  if (e == hipSuccess)
+    e = launch_attention_varlen(s->dtype, s->d, true, Q, K, ws, B, seqs.data(), s->Hq, s->Hkv, X, Y, st);
+  return hip_status(e);
+}
+
+int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, const void* Q, const void* K,
+                     const void* V, const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes,
+                     void* stream) {
+  TSA_TRY(check_varlen(s, B, cu_seqlens));
+  TSA_TRY(need_ptrs({Q, K, V, Y}));
+  TSA_TRY(opt_ptrs({X}));
+  if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
+  const VarlenWs w = varlen_layout(s, B, cu_seqlens);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  hipStream_t st = stream_of(stream);
+  const StageWs& g = w.st;
+  const size_t eb = elem_bytes(s->dtype), Hq = s->Hq, Hkv = s->Hkv, d = s->d;
+  int32_t* kLp = at<int32_t>(ws, w.kLp);
+  std::vector<int64_t> P(B + 1, 0);
+  for (int32_t b = 0; b < B; ++b) P[b + 1] = P[b] + tsa_capacity(cu_seqlens[b + 1] - cu_seqlens[b]);
+  auto tok = [&](const void* base, size_t heads, int32_t b) {
+    return static_cast<const char*>(base) + (size_t)cu_seqlens[b] * heads * d * eb;
+  };
+  auto comp = [&](size_t off, int32_t b) { return at<char>(ws, off) + (size_t)P[b] * Hq * d * eb; };
+  hipError_t e = hipSuccess;
+  // stages 1-4a sample by sample (each O(L_b)); the stage workspace is reused in stream order
+  for (int32_t b = 0; b < B && e == hipSuccess; ++b) {
+    const int64_t Lb = cu_seqlens[b + 1] - cu_seqlens[b], Cb = P[b + 1] - P[b];
+    float* s_h = at<float>(ws, w.s_h) + Hq * (size_t)P[b];
+    float* s_l = at<float>(ws, w.s_l) + (size_t)P[b];
+    int32_t* idx = at<int32_t>(ws, w.idx) + Hq * (size_t)P[b];
+    int32_t* inv = at<int32_t>(ws, w.inv) + Hq * (size_t)P[b];
+    int32_t* kl = kLp + 2 * b;
+    e = launch_fill_zero(at<char>(ws, g.bhist), g.kLp - g.bhist, st);
+    if (e == hipSuccess) e = launch_fill_zero(at<char>(ws, g.shist), g.tcnt - g.shist, st);
+    if (e == hipSuccess)
+      e = launch_score(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), Lb, s->Hq, s->Hkv, s->q, s_h,
+                       at<double2>(ws, g.partials), at<double2>(ws, g.rowstat), st);
+    if (e == hipSuccess) e = launch_layer_score(s_h, Lb, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l, st);
+    if (e == hipSuccess)
+      e = launch_budget(s_l, Lb, budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl), kl,
+                        kLp_dev ? kLp_dev + 2 * b : nullptr, kLp_dev ? kLp_dev + 2 * b + 1 : nullptr, st);
+    if (e == hipSuccess)
+      e = launch_select(s_h, Lb, s->Hq, kl + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
+                        at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
+    if (e == hipSuccess)
+      e = launch_gather(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), tok(V, Hkv, b), idx, kl + 1, Lb, s->Hq,
+                        s->Hkv, Cb, comp(w.Qh, b), comp(w.Kh, b), comp(w.Vht, b), st);
+  }
+  // stage 4b: one launch over every sample's ragged L'_b
+  if (e == hipSuccess) {
+    std::vector<AttnSeqDesc> seqs;
+    for (int32_t b : longest_first(B, cu_seqlens))
+      seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], kLp + 2 * b + 1});
+    e = launch_attention_varlen(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
+                                B, seqs.data(), s->Hq, s->Hkv, nullptr, at<void>(ws, w.Oh), st);
+  }
+  // stage 5 sample by sample
+  for (int32_t b = 0; b < B && e == hipSuccess; ++b) {
+    const int64_t Lb = cu_seqlens[b + 1] - cu_seqlens[b], Cb = P[b + 1] - P[b];
+    const size_t row = (size_t)cu_seqlens[b] * Hq * d * eb;
+    e = launch_scatter(s->dtype, s->d, comp(w.Oh, b), at<int32_t>(ws, w.idx) + Hq * (size_t)P[b],
+                       at<int32_t>(ws, w.inv) + Hq * (size_t)P[b], kLp + 2 * b + 1,
+                       X ? static_cast<const char*>(X) + row : nullptr, static_cast<char*>(Y) + row, Lb, s->Hq, Cb, st);
+  }
   return hip_status(e);
 }
 

@@ -27,22 +27,44 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-struct AttnArgs {
-  const void* Q;        // compressed: Qh [Hq][C][d];  dense: Q [L][Hq][d]
-  const void* K;        // compressed: Kh [Hq][C][d];  dense: K [L][Hkv][d]
-  const void* Vt;       // compressed: Vht [Hq][d][C]; dense: Vt [Hkv][d][C]
-  const int32_t* Lp_dev;
-  const void* X;        // dense only: residual [L][Hq][d] or null
-  void* O;              // compressed: Oh [Hq][C][d];  dense: Y [L][Hq][d]
-  int64_t L, C;
-  int Hq, Hkv;
-  float scale;
+// One sequence of a launch.  A launch covers up to kMaxSeg sequences packed along the token
+// dimension (a varlen batch; a single sequence is the one-segment case), each with its own length
+// and, in the compressed case, its own keep count L' on the device.
+constexpr int kMaxSeg = 32;
+struct AttnSeg {
+  int64_t tok_off;      // dense: first token of the sequence in Q, K, X and Y
+  int64_t cap_off;      // first row of the sequence's region in the capacity-strided tensors
+  int64_t L;            // dense: sequence length
+  int64_t C;            // capacity of the sequence's region (multiple of 256, >= L)
+  const int32_t* Lp;    // compressed: device keep count L'
+  int32_t blk0;         // first block of the sequence in the grid
+  int32_t nmb;          // query blocks per head
 };
 
-// blockIdx -> (head, query block), heavy (late) query blocks first.
-__device__ __forceinline__ void block_coords(int nmb, int Hq, int& h, int& mb) {
-  const int b = blockIdx.x;
-  if ((Hq & 7) == 0) {
+// Compressed: the region of sequence s in Qh, Kh, Oh is [Hq][C][d] and in Vht [Hq][d][C], starting
+// at element Hq * d * cap_off.  Dense: Q, X, Y [tokens][Hq][d], K [tokens][Hkv][d] from token
+// tok_off on; Vt [Hkv][d][C] (V transposed) from element Hkv * d * cap_off on.
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* Vt;
+  const void* X;        // dense only: residual or null
+  void* O;
+  int Hq, Hkv;
+  float scale;
+  int nseg;
+  AttnSeg seg[kMaxSeg];
+};
+
+// blockIdx -> (segment, head, query block), heavy (late) query blocks first within a head.  Every
+// segment starts at a multiple of 8 blocks when Hq % 8 == 0, so blockIdx % 8 (the XCD a block runs
+// on) also numbers the heads of one 8-head group: consecutive blocks of one XCD share a head.
+__device__ __forceinline__ const AttnSeg& block_coords(const AttnArgs& a, int& h, int& mb) {
+  int si = 0;
+  while (si + 1 < a.nseg && (int)blockIdx.x >= a.seg[si + 1].blk0) ++si;
+  const AttnSeg& sg = a.seg[si];
+  const int b = (int)blockIdx.x - sg.blk0, nmb = sg.nmb;
+  if ((a.Hq & 7) == 0) {
     const int xcd = b & 7, slot = b >> 3;
     h = (slot / nmb) * 8 + xcd;
     mb = nmb - 1 - slot % nmb;
@@ -50,6 +72,7 @@ __device__ __forceinline__ void block_coords(int nmb, int Hq, int& h, int& mb) {
     h = b / nmb;
     mb = nmb - 1 - b % nmb;
   }
+  return sg;
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -97,22 +120,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   // LDS: K slots 0,1 then V slots 0,1
   __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * VTILE];
 
-  const int nmb = (int)((a.L + BM - 1) / BM);
   int h, mb;
-  block_coords(nmb, a.Hq, h, mb);
-  const int Lp = DENSE ? (int)a.L : a.Lp_dev[0];
+  const AttnSeg& sg = block_coords(a, h, mb);
+  const int Lp = DENSE ? (int)sg.L : sg.Lp[0];
   const int m0 = mb * BM;
   if (m0 >= Lp) return;
 
   const int tid = threadIdx.x, lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = h / (a.Hq / a.Hkv);
+  const int64_t C = sg.C;
   const uint32_t q_rs = DENSE ? a.Hq * D * 2 : D * 2;
   const uint32_t k_rs = DENSE ? a.Hkv * D * 2 : D * 2;
-  const uint32_t v_rs = (uint32_t)a.C * 2;
-  const char* qbase = static_cast<const char*>(a.Q) + (DENSE ? (size_t)h * D * 2 : (size_t)h * a.C * D * 2);
-  const char* kbase = static_cast<const char*>(a.K) + (DENSE ? (size_t)g * D * 2 : (size_t)h * a.C * D * 2);
-  const char* vbase = static_cast<const char*>(a.Vt) + (size_t)(DENSE ? g : h) * D * a.C * 2;
+  const uint32_t v_rs = (uint32_t)C * 2;
+  // element offsets of this (sequence, head) in Q/O, K and V^T
+  const size_t qo_off = DENSE ? ((size_t)sg.tok_off * a.Hq + h) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
+  const size_t k_off = DENSE ? ((size_t)sg.tok_off * a.Hkv + g) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
+  const size_t v_off = (size_t)sg.cap_off * (DENSE ? a.Hkv : a.Hq) * D + (size_t)(DENSE ? g : h) * D * C;
+  const char* qbase = static_cast<const char*>(a.Q) + qo_off * 2;
+  const char* kbase = static_cast<const char*>(a.K) + k_off * 2;
+  const char* vbase = static_cast<const char*>(a.Vt) + v_off * 2;
 
   const int qi = m0 + 32 * w + ln;      // this lane's query row
   bf16x8_t qf[KS];
@@ -281,10 +308,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (qi >= Lp) return;
   const float inv_l = 1.f / l_tot;
-  char* obase = static_cast<char*>(a.O) + (DENSE ? (size_t)h * D * 2 : (size_t)h * a.C * D * 2);
-  uint16_t* orow = reinterpret_cast<uint16_t*>(obase + (size_t)qi * q_rs);
+  uint16_t* orow = reinterpret_cast<uint16_t*>(static_cast<char*>(a.O) + qo_off * 2 + (size_t)qi * q_rs);
   const uint16_t* xrow = DENSE && a.X
-      ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.X) + (size_t)h * D * 2 + (size_t)qi * q_rs)
+      ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.X) + qo_off * 2 + (size_t)qi * q_rs)
       : nullptr;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -316,21 +342,25 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int TPR = 4, BM = 256 / TPR, BN = 32, DPT = D / TPR;
   __shared__ float smK[BN][D + 1];
   __shared__ float smV[BN][D + 1];
-  const int nmb = (int)((a.L + BM - 1) / BM);
   int h, mb;
-  block_coords(nmb, a.Hq, h, mb);
-  const int64_t Lp = DENSE ? a.L : (int64_t)a.Lp_dev[0];
+  const AttnSeg& sg = block_coords(a, h, mb);
+  const int64_t Lp = DENSE ? sg.L : (int64_t)sg.Lp[0];
   const int64_t m0 = (int64_t)mb * BM;
   if (m0 >= Lp) return;
   const int tid = threadIdx.x, part = tid % TPR;
   const int64_t qi = m0 + tid / TPR;
   const int g = h / (a.Hq / a.Hkv);
+  const int64_t C = sg.C;
   const float* Qp = static_cast<const float*>(a.Q);
   const float* Kp = static_cast<const float*>(a.K);
   const float* Vp = static_cast<const float*>(a.Vt);
-  auto q_row = [&](int64_t i) -> size_t { return DENSE ? ((size_t)i * a.Hq + h) * D : ((size_t)h * a.C + i) * D; };
-  auto k_row = [&](int64_t j) -> size_t { return DENSE ? ((size_t)j * a.Hkv + g) * D : ((size_t)h * a.C + j) * D; };
-  const size_t v_base = (size_t)(DENSE ? g : h) * D * a.C;
+  auto q_row = [&](int64_t i) -> size_t {
+    return DENSE ? ((size_t)(sg.tok_off + i) * a.Hq + h) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C + i) * D;
+  };
+  auto k_row = [&](int64_t j) -> size_t {
+    return DENSE ? ((size_t)(sg.tok_off + j) * a.Hkv + g) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C + j) * D;
+  };
+  const size_t v_base = (size_t)sg.cap_off * (DENSE ? a.Hkv : a.Hq) * D + (size_t)(DENSE ? g : h) * D * C;
 
   float qr[DPT], acc[DPT];
 #pragma unroll
@@ -347,7 +377,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       const int64_t j = key0 + r;
       smK[r][c] = j < Lp ? Kp[k_row(j) + c] : 0.f;
       const int cv = e / BN, rv = e % BN;           // V^T is token-fastest: coalesce along keys
-      smV[rv][cv] = key0 + rv < Lp ? Vp[v_base + (size_t)cv * a.C + key0 + rv] : 0.f;
+      smV[rv][cv] = key0 + rv < Lp ? Vp[v_base + (size_t)cv * C + key0 + rv] : 0.f;
     }
     __syncthreads();
     float sc[BN];
@@ -391,23 +421,45 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 template <int D, bool DENSE>
-static hipError_t run_attn(int dtype, const AttnArgs& a, hipStream_t st) {
-  if (dtype == 1) {
-    const int nmb = (int)((a.L + 127) / 128);
-    attn_bf16_kernel<D, DENSE><<<(unsigned)(nmb * a.Hq), 256, 0, st>>>(a);
-  } else {
-    const int nmb = (int)((a.L + 63) / 64);
-    attn_f32_kernel<D, DENSE><<<(unsigned)(nmb * a.Hq), 256, 0, st>>>(a);
-  }
+static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st) {
+  if (dtype == 1)
+    attn_bf16_kernel<D, DENSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
+  else
+    attn_f32_kernel<D, DENSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, const void* K, const void* Vt,
+                                   int nseq, const AttnSeqDesc* seqs, int Hq, int Hkv, const void* X, void* O,
+                                   hipStream_t st) {
+  const int bm = dtype == 1 ? 128 : 64;        // query rows per block
+  AttnArgs a{};
+  a.Q = Q; a.K = K; a.Vt = Vt; a.X = X; a.O = O;
+  a.Hq = Hq; a.Hkv = Hkv; a.scale = (float)(1.0 / sqrt((double)d));
+  for (int first = 0; first < nseq; first += kMaxSeg) {
+    a.nseg = nseq - first < kMaxSeg ? nseq - first : kMaxSeg;
+    int nblocks = 0;
+    for (int i = 0; i < a.nseg; ++i) {
+      const AttnSeqDesc& q = seqs[first + i];
+      AttnSeg& g = a.seg[i];
+      g.tok_off = q.tok_off; g.cap_off = q.cap_off; g.L = q.L; g.C = q.C; g.Lp = q.Lp_dev;
+      g.blk0 = nblocks;
+      g.nmb = (int)((q.L + bm - 1) / bm);
+      nblocks += g.nmb * Hq;
+    }
+    hipError_t e;
+    if (d == 128) e = dense ? run_attn<128, true>(dtype, a, nblocks, st) : run_attn<128, false>(dtype, a, nblocks, st);
+    else e = dense ? run_attn<64, true>(dtype, a, nblocks, st) : run_attn<64, false>(dtype, a, nblocks, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const void* K,
                             const void* Vt, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
                             int64_t C, const void* X, void* O, hipStream_t st) {
-  AttnArgs a{Q, K, Vt, Lp_dev, X, O, L, C, Hq, Hkv, (float)(1.0 / sqrt((double)d))};
-  if (d == 128) return dense ? run_attn<128, true>(dtype, a, st) : run_attn<128, false>(dtype, a, st);
-  return dense ? run_attn<64, true>(dtype, a, st) : run_attn<64, false>(dtype, a, st);
+  const AttnSeqDesc one{0, 0, L, C, Lp_dev};
+  return launch_attention_varlen(dtype, d, dense, Q, K, Vt, 1, &one, Hq, Hkv, X, O, st);
 }
 
 }  // namespace tsa

@@ -21,9 +21,9 @@ int64_t score_blocks(int64_t L) { return (L + kScoreKeys - 1) / kScoreKeys; }
 
 size_t score_partial_bytes(int64_t L, int Hq, int q) {
   // float64 path: a partial per row, 256-key block and wave; matrix-core path: a partial per padded
-  // row and 1024-key block (at most 16 * Hq * ceil(q/16) rows)
+  // row and block of at least 256 keys (at most 16 * Hq * ceil(q/16) rows)
   const size_t vec = (size_t)Hq * q * score_blocks(L) * (kScoreKeys / kWave);
-  const size_t mfma = (size_t)Hq * ((q + 15) / 16 * 16) * ((L + 1023) / 1024);
+  const size_t mfma = (size_t)Hq * ((q + 15) / 16 * 16) * ((L + 255) / 256);
   return (vec > mfma ? vec : mfma) * sizeof(double2);
 }
 
@@ -182,7 +182,7 @@ static hipError_t run_score(const void* Q, const void* K, int64_t L, int Hq, int
 // Every exponential is exp2 of (z - m) * log2(e) / sqrt(d) formed in float64 from the float32
 // logits, evaluated as exp2f(hi) * (1 + lo * ln 2) with hi + lo that argument, and all sums are
 // float64: about 1e-7 relative, far inside the selection's 1e-6 tie band.
-constexpr int kMKeys = 1024, kMSub = 256, kMRows = 256;   // keys per block / per sub-chunk; max rows
+constexpr int kMSub = 256, kMRows = 256;   // keys per sub-chunk (a block walks nsub of them); max rows
 
 typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
 typedef float f32x4s_t __attribute__((ext_vector_type(4)));
@@ -207,9 +207,9 @@ __device__ __forceinline__ float shfl_max16(float v) {
 
 template <int D, int PASS>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                         int64_t L, int Hq, int Hkv, int q, int qp, double c,
-                                                         double2* __restrict__ part, const double2* __restrict__ rowstat,
-                                                         float* __restrict__ s_h) {
+                                                         int64_t L, int Hq, int Hkv, int q, int qp, int nsub,
+                                                         double c, double2* __restrict__ part,
+                                                         const double2* __restrict__ rowstat, float* __restrict__ s_h) {
   constexpr int KST = D / 32;                  // K-steps of 32 over the head dim
   __shared__ __attribute__((aligned(16))) uint16_t qs[kMRows * D];
   __shared__ float wm[4][kMRows];              // pass 1: per-wave partial max ...
@@ -239,9 +239,10 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restr
 
   // Blocks whose keys all precede the recent window, with every padded row real (q % 16 == 0), see
   // every key from every row: no masks.
-  const bool open = (int64_t)(blockIdx.x + 1) * kMKeys <= L - q + 1 && q == qp;
-  for (int sub = 0; sub < kMKeys / kMSub; ++sub) {
-    const int64_t key0 = ((int64_t)blockIdx.x * kMKeys + sub * kMSub) + 64 * w;
+  const int64_t bkeys = (int64_t)nsub * kMSub;
+  const bool open = (int64_t)(blockIdx.x + 1) * bkeys <= L - q + 1 && q == qp;
+  for (int sub = 0; sub < nsub; ++sub) {
+    const int64_t key0 = ((int64_t)blockIdx.x * bkeys + sub * kMSub) + 64 * w;
     bf16x8s_t kf[4][KST];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -352,13 +353,16 @@ static hipError_t run_score_mfma(const void* Q, const void* K, int64_t L, int Hq
                                  double2* part, double2* rowstat, hipStream_t st) {
   const int qp = (q + 15) / 16 * 16, Rp = score_rows_padded(Hq, Hkv, q);
   const double scale = 1.0 / sqrt((double)D), c = scale * 1.4426950408889634;
-  const dim3 grid((unsigned)((L + kMKeys - 1) / kMKeys), (unsigned)Hkv);
+  // keys per block: 1024 when that still gives ~2 blocks per CU, down to 256 for short sequences
+  int nsub = 4;
+  while (nsub > 1 && ((L + nsub * kMSub - 1) / (nsub * kMSub)) * Hkv < 512) nsub >>= 1;
+  const dim3 grid((unsigned)((L + nsub * kMSub - 1) / (nsub * kMSub)), (unsigned)Hkv);
   const uint16_t* Qt = static_cast<const uint16_t*>(Q);
   const uint16_t* Kt = static_cast<const uint16_t*>(K);
-  score_mfma_kernel<D, 1><<<grid, 256, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, c, part, rowstat, s_h);
+  score_mfma_kernel<D, 1><<<grid, 256, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
   const int64_t nrows = (int64_t)Hkv * Rp;
   score_combine_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(part, nrows, grid.x, scale, rowstat);
-  score_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, c, part, rowstat, s_h);
+  score_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
   return hipGetLastError();
 }
 

@@ -16,57 +16,67 @@
 
 namespace tsa {
 
-constexpr int kLayerTile = 1024;
+constexpr int kLayerTile = 256;      // tokens per block in the layer-score kernels
 constexpr int kSelTile = 2048;     // elements per block in the compaction kernels
 constexpr int kHistTile = 4096;    // elements per block in the histogram kernels
 constexpr double kTwo60 = 1152921504606846976.0;
 
-int64_t layer_tiles(int64_t L) { return (L + kLayerTile - 1) / kLayerTile; }
+// tile sums plus one slot for their total
+int64_t layer_tiles(int64_t L) { return (L + kLayerTile - 1) / kLayerTile + 1; }
 int64_t select_tiles(int64_t L) { return (L + kSelTile - 1) / kSelTile; }
 
 // ---- layer score --------------------------------------------------------------------------------
+// S[t] = sum over heads in head order (float64); s_l = S / total with the total summed once, in a
+// fixed order, by a single block.  One token per thread, so a launch has L/256 blocks.
 
 __global__ __launch_bounds__(256) void layer_sum_kernel(const float* __restrict__ s_h, int64_t L, int Hq,
                                                         double* __restrict__ S, double* __restrict__ tile_sum) {
   __shared__ double red[4];
-  double local = 0.0;
-  for (int u = 0; u < kLayerTile / 256; ++u) {
-    const int64_t t = (int64_t)blockIdx.x * kLayerTile + u * 256 + threadIdx.x;
-    if (t < L) {
-      double acc = 0.0;
-      for (int h = 0; h < Hq; ++h) acc += (double)s_h[(size_t)h * L + t];
-      S[t] = acc;
-      local += acc;
+  const int64_t t = (int64_t)blockIdx.x * kLayerTile + threadIdx.x;
+  double acc = 0.0;
+  if (t < L) {
+    int h = 0;
+    for (; h + 8 <= Hq; h += 8) {       // loads first, then the adds in head order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = s_h[(size_t)(h + u) * L + t];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += (double)v[u];
     }
+    for (; h < Hq; ++h) acc += (double)s_h[(size_t)h * L + t];
+    S[t] = acc;
   }
-  local = wave_sum(local);
+  const double local = wave_sum(acc);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local;
   __syncthreads();
   if (threadIdx.x == 0) tile_sum[blockIdx.x] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__global__ __launch_bounds__(256) void layer_norm_kernel(const double* __restrict__ S,
-                                                         const double* __restrict__ tile_sum,
-                                                         int64_t ntiles, int64_t L, float* __restrict__ s_l) {
-  __shared__ double total;
-  if (threadIdx.x < 64) {
-    double a = 0.0;
-    for (int64_t i = threadIdx.x; i < ntiles; i += 64) a += tile_sum[i];
-    a = wave_sum(a);
-    if (threadIdx.x == 0) total = a;
-  }
+// total = sum of the tile sums (fixed order: strided per-thread partials, then a fixed tree),
+// stored after them at tile_sum[ntiles].
+__global__ __launch_bounds__(256) void layer_total_kernel(double* __restrict__ tile_sum, int64_t ntiles) {
+  __shared__ double red[4];
+  double a = 0.0;
+  for (int64_t i = threadIdx.x; i < ntiles; i += 256) a += tile_sum[i];
+  a = wave_sum(a);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
   __syncthreads();
-  for (int u = 0; u < kLayerTile / 256; ++u) {
-    const int64_t t = (int64_t)blockIdx.x * kLayerTile + u * 256 + threadIdx.x;
-    if (t < L) s_l[t] = (float)(S[t] / total);
-  }
+  if (threadIdx.x == 0) tile_sum[ntiles] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+__global__ __launch_bounds__(256) void layer_norm_kernel(const double* __restrict__ S,
+                                                         const double* __restrict__ total, int64_t L,
+                                                         float* __restrict__ s_l) {
+  const int64_t t = (int64_t)blockIdx.x * kLayerTile + threadIdx.x;
+  if (t < L) s_l[t] = (float)(S[t] / total[0]);
 }
 
 hipError_t launch_layer_score(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum,
                               float* s_l, hipStream_t st) {
-  const unsigned n = (unsigned)layer_tiles(L);
+  const unsigned n = (unsigned)(layer_tiles(L) - 1);
   layer_sum_kernel<<<n, 256, 0, st>>>(s_h, L, Hq, S, tile_sum);
-  layer_norm_kernel<<<n, 256, 0, st>>>(S, tile_sum, n, L, s_l);
+  layer_total_kernel<<<1, 256, 0, st>>>(tile_sum, n);
+  layer_norm_kernel<<<n, 256, 0, st>>>(S, tile_sum + n, L, s_l);
   return hipGetLastError();
 }
 

@@ -62,4 +62,16 @@ hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const v
                             const void* Vt, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
                             int64_t C, const void* X, void* O, hipStream_t st);
 
+// One sequence of a varlen batch.  Compressed: its Qh/Kh/Oh region [Hq][C][d] and Vht region
+// [Hq][d][C] start at element Hq*d*cap_off, L' is read from Lp_dev, and L bounds the grid (L' <= L).
+// Dense: tokens [tok_off, tok_off + L) of Q/K/X/Y; its Vt region [Hkv][d][C] starts at element
+// Hkv*d*cap_off.  Longer sequences listed first are scheduled first.
+struct AttnSeqDesc {
+  int64_t tok_off, cap_off, L, C;
+  const int32_t* Lp_dev;
+};
+hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, const void* K, const void* Vt,
+                                   int nseq, const AttnSeqDesc* seqs, int Hq, int Hkv, const void* X, void* O,
+                                   hipStream_t st);
+
 }  // namespace tsa

@@ -16,12 +16,14 @@ Recipe (all draws from ``numpy.random.Generator(PCG64(seed))``, in this order):
    head in group g get Q[p, h] += 2 u_g; with ``sink`` > 0 the first ``sink`` keys get K += 2 u_g.
 5. Storage rounding: bf16 workloads round every tensor to bfloat16 (round to nearest even, via
    torch); fp32 workloads keep the fp32 draws.
+6. Varlen batches: sample b is an independent draw of the same recipe at its own length, seeded by
+   the b-th child of SeedSequence(seed + 2000); samples are packed along the token axis.
 """
 
 import numpy as np
 import torch
 
-from .configs import Workload
+from .configs import Workload, scaled
 
 
 def _salient_sets(rng, cfg: Workload, prev=None):
@@ -94,3 +96,15 @@ def iter_chain(cfg: Workload):
         lay = make_layer(cfg, seed=s, with_x=(i == 0), prev_sets=prev)
         prev = lay["sets"]
         yield i + 1, lay
+
+
+def make_batch(cfg: Workload, lengths, seed=None):
+    """A varlen batch: one independent draw of `cfg`'s recipe per sample length, packed along the
+    token axis.  Returns the packed CPU tensors, cu_seqlens (B+1 offsets) and the per-sample draws."""
+    ss = np.random.SeedSequence(cfg.seed + 2000 if seed is None else seed).spawn(len(lengths))
+    parts = [make_layer(scaled(cfg, int(L)), seed=int(s.generate_state(1)[0])) for L, s in zip(lengths, ss)]
+    cu = np.concatenate([[0], np.cumsum([int(L) for L in lengths])]).astype(np.int64)
+    out = {n: torch.cat([p[n] for p in parts], dim=0) for n in ("Q", "K", "V", "X")}
+    out["cu_seqlens"] = cu
+    out["parts"] = parts
+    return out
