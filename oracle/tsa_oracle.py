@@ -30,6 +30,13 @@ R5  GQA: query head h reads KV head floor(h / (Hq / Hkv)); head h is ranked by i
 R6  Compressed attention is causal by ORIGINAL positions (S_h[j] <= S_h[i]) with scale 1/sqrt(d).
 R7  Decompress writes +0.0 into unselected rows; the residual is Y = X + Decompress(O_hat) per head,
     with no output projection.
+R11 Block sparsity inside the compressed space (the pages stack a block-sparse kernel after the
+    token filter but describe no block rule of their own): blocks of 128 compressed rows; each
+    block's Q_hat and K_hat rows are mean-pooled (sum in float64, divide, round once to float32);
+    query block I weighs its causal key blocks J <= I by softmax_J(<qbar_I, kbar_J> / sqrt(d)) and
+    keeps the fewest heaviest blocks (ties: lower J) whose weight reaches gamma (all when gamma >= 1
+    or when no prefix reaches it), plus block 0 and the diagonal block I; attention then sees only
+    the kept blocks, causally inside the diagonal block.
 R10 Fixed-ratio budget (the ablation baseline): the pruned count k is s*L rounded to the nearest
     integer, halves rounded up, on the exact value of the stored float32 ratio s; L' = L - k.
 """
@@ -191,6 +198,80 @@ def decompress(Oh, idx, L):
 def residual(X, O):
     """X_{l+1} = X_l + Decompress(O_hat) (notes, Key design 1; summary, Core Architecture)."""
     return X + O
+
+
+# -- Block sparsity stacked on the token selection --------------------------------------------------
+
+BLOCK = 128
+
+
+def block_pool(Xh, Lp, B=BLOCK):
+    """Mean of every block of B consecutive compressed rows of one head (the last block over its
+    valid rows), summed row by row in float64 and rounded once to float32 (reading R11).
+
+    notes, Key findings and blog 3.2: token selection first, then block-level sparse attention on the
+    compressed, contiguous Q_hat K_hat V_hat.  Xh: [>= L'][d].  Returns [ceil(L'/B)][d] float64
+    holding float32 values."""
+    nb = -(-Lp // B)
+    out = np.zeros((nb, Xh.shape[1]))
+    for b in range(nb):
+        acc = np.zeros(Xh.shape[1])
+        rows = range(b * B, min(Lp, (b + 1) * B))
+        for r in rows:
+            acc = acc + Xh[r]
+        out[b] = (acc / len(rows)).astype(np.float32)
+    return out
+
+
+def block_select(qbar, kbar, gamma):
+    """Kept key blocks of every query block (reading R11), each ascending.
+
+    For query block I: weights a_J = softmax over J <= I of <qbar_I, kbar_J> / sqrt(d); order J by
+    (a_J descending, J ascending) and take the shortest prefix whose cumulative weight reaches gamma
+    (every J when gamma >= 1 or no prefix does); add J = 0 and J = I."""
+    nb, d = qbar.shape
+    keep = []
+    for I in range(nb):
+        z = (kbar[: I + 1] @ qbar[I]) / np.sqrt(d)
+        a = np.exp(z - z.max())
+        a = a / a.sum()
+        order = np.lexsort((np.arange(I + 1), -a))
+        cum = np.cumsum(a[order])
+        hit = np.nonzero(cum >= gamma)[0]
+        n = int(hit[0]) + 1 if (gamma < 1 and len(hit)) else I + 1
+        keep.append(np.array(sorted(set(order[:n].tolist()) | {0, I}), dtype=np.int64))
+    return keep
+
+
+def block_sparse_attention_rows(Qh, Kh, Vh, keep, rows=None, B=BLOCK):
+    """Causal attention of one head in the compressed space where row i (query block i // B) sees
+    only keys j <= i inside its kept key blocks (reading R11)."""
+    n, d = Qh.shape
+    rows = np.arange(n) if rows is None else np.asarray(rows)
+    out = np.zeros((len(rows), Vh.shape[1]))
+    for o, i in enumerate(rows):
+        blocks = keep[i // B]
+        j = np.concatenate([np.arange(J * B, min((J + 1) * B, n)) for J in blocks])
+        j = j[j <= i]
+        z = Kh[j] @ Qh[i] / np.sqrt(d)
+        e = np.exp(z - z.max())
+        out[o] = (e / e.sum()) @ Vh[j]
+    return out
+
+
+def block_sparse_layer(Q, K, V, X, tau, q, gamma):
+    """The token-sparse layer with block sparsity inside the compressed attention."""
+    L = Q.shape[0]
+    s_h = head_scores(Q, K, q)
+    s_l = layer_score(s_h)
+    k, Lp = budget(s_l, tau)
+    idx = select(s_h, Lp)
+    Qh, Kh, Vh = gather(Q, K, V, idx)
+    keep = [block_select(block_pool(Qh[h], Lp), block_pool(Kh[h], Lp), gamma) for h in range(Qh.shape[0])]
+    Oh = np.stack([block_sparse_attention_rows(Qh[h], Kh[h], Vh[h], keep[h]) for h in range(Qh.shape[0])])
+    O = decompress(Oh, idx, L)
+    Y = residual(X, O) if X is not None else O
+    return dict(s_h=s_h, s_l=s_l, k=k, Lp=Lp, idx=idx, keep=keep, Oh=Oh, Y=Y)
 
 
 # -- The whole layer and its dense counterpart ----------------------------------------------------

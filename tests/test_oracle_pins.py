@@ -360,6 +360,106 @@ def test_varlen_batch_keeps_samples_apart():
     assert np.array_equal(Y2[keep], Y[keep]) and not np.array_equal(Y2[cu[2]:cu[3]], Y[cu[2]:cu[3]])
 
 
+# -- block sparsity in the compressed space (reading R11) -------------------------------------------
+
+def _bf16_values(shape, seed):
+    return oracle.round_to_storage(np.random.default_rng(seed).standard_normal(shape), "bf16")
+
+
+def test_block_pool_is_the_block_mean():
+    """bf16 values sum exactly in float64, so the pool equals the library's reshaped mean rounded
+    to float32; the last, partial block averages only its own rows."""
+    X = _bf16_values((300, 16), 3)
+    got = oracle.block_pool(X, 256)
+    want = X[:256].reshape(2, 128, 16).mean(axis=1).astype(np.float32)
+    assert np.array_equal(got, want)
+    got = oracle.block_pool(X, 300)
+    assert got.shape == (3, 16) and np.array_equal(got[2], X[256:300].mean(axis=0).astype(np.float32))
+    assert oracle.block_pool(X, 0).shape == (0, 16)
+
+
+def test_block_select_hand_case():
+    """Weights 0.6 / 0.1 / 0.3 on key blocks 0 / 1 / 2 for query block 2 (kbar chosen so that the
+    scaled logits are ln 6, ln 1, ln 3)."""
+    d = 4
+    kbar = np.zeros((3, d))
+    kbar[:, 0] = 2 * np.log([6.0, 1.0, 3.0])          # <qbar, kbar> / sqrt(4) = ln w
+    qbar = np.zeros((3, d))
+    qbar[:, 0] = 1.0
+    keep = oracle.block_select(qbar, kbar, gamma=0.5)
+    assert [k.tolist() for k in keep] == [[0], [0, 1], [0, 2]]   # block 2: 0 reaches 0.6, 2 forced
+    keep = oracle.block_select(qbar, kbar, gamma=0.65)
+    assert keep[2].tolist() == [0, 2]                 # 0.6 + 0.3
+    keep = oracle.block_select(qbar, kbar, gamma=0.95)
+    assert keep[2].tolist() == [0, 1, 2]
+    keep = oracle.block_select(qbar, kbar, gamma=1.0)
+    assert keep[2].tolist() == [0, 1, 2]
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_block_select_is_the_fewest_heaviest_blocks(seed):
+    """Brute force over every subset of candidate blocks: the non-forced part of the kept set has the
+    minimum size of any subset reaching gamma and the largest weight among subsets of that size."""
+    rng = np.random.default_rng(seed)
+    nb, d = 9, 8
+    qbar, kbar = rng.standard_normal((nb, d)) * 2, rng.standard_normal((nb, d)) * 2
+    for gamma in (0.3, 0.7, 0.9):
+        keep = oracle.block_select(qbar, kbar, gamma)
+        for I in range(nb):
+            z = kbar[: I + 1] @ qbar[I] / np.sqrt(d)
+            a = np.exp(z - z.max())
+            a /= a.sum()
+            best_n, best_w = None, None
+            for n in range(1, I + 2):
+                w = max(sum(a[list(c)]) for c in itertools.combinations(range(I + 1), n))
+                if w >= gamma:
+                    best_n, best_w = n, w
+                    break
+            forced = {0, I}
+            k = set(keep[I].tolist())
+            assert forced <= k
+            # the greedy prefix: best_n heaviest blocks (ties impossible with continuous draws)
+            top = set(np.argsort(-a, kind="stable")[:best_n].tolist())
+            assert k == top | forced, (gamma, I)
+            assert abs(sum(a[list(top)]) - best_w) < 1e-12
+
+
+def test_block_sparse_attention_matches_masked_library_attention():
+    """Kept-block attention equals the library's attention under the explicit boolean mask
+    (causal and inside a kept block), small blocks for many of them."""
+    rng = np.random.default_rng(9)
+    n, d, B = 100, 16, 16
+    Qh, Kh, Vh = (rng.standard_normal((n, d)) for _ in range(3))
+    nb = -(-n // B)
+    keep = [np.array(sorted({0, I} | set(rng.choice(I + 1, size=min(I + 1, 2), replace=False).tolist())))
+            for I in range(nb)]
+    M = np.zeros((n, n), dtype=bool)
+    for i in range(n):
+        for J in keep[i // B]:
+            M[i, J * B: min((J + 1) * B, n)] = True
+    M &= np.tril(np.ones((n, n), dtype=bool))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(Qh)[None], torch.from_numpy(Kh)[None], torch.from_numpy(Vh)[None],
+        attn_mask=torch.from_numpy(M)[None]).numpy()[0]
+    got = oracle.block_sparse_attention_rows(Qh, Kh, Vh, keep, B=B)
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    full = [np.arange(I + 1) for I in range(nb)]
+    assert np.allclose(oracle.block_sparse_attention_rows(Qh, Kh, Vh, full, B=B),
+                       oracle.attention_rows(Qh, Kh, Vh, np.arange(n)), rtol=1e-13, atol=1e-13)
+
+
+def test_block_sparse_layer_with_full_coverage_is_the_layer():
+    rng = np.random.default_rng(12)
+    L, Hq, Hkv, d, q = 700, 2, 1, 16, 4
+    Q, K, V, X = (rng.standard_normal(sh) for sh in ((L, Hq, d), (L, Hkv, d), (L, Hkv, d), (L, Hq, d)))
+    a = oracle.layer(Q, K, V, X, tau=0.1, q=q)
+    b = oracle.block_sparse_layer(Q, K, V, X, tau=0.1, q=q, gamma=1.0)
+    assert all(len(k) == I + 1 for kh in b["keep"] for I, k in enumerate(kh))
+    assert np.allclose(b["Y"], a["Y"], rtol=1e-13, atol=1e-13)
+    c = oracle.block_sparse_layer(Q, K, V, X, tau=0.1, q=q, gamma=0.2)
+    assert sum(len(k) for kh in c["keep"] for k in kh) < sum(len(k) for kh in b["keep"] for k in kh)
+
+
 def test_sparse_layers_and_drift():
     R = [0.4, 0.3, 0.5, 0.1, 0.2, 0.05, 0.45, 0.35]
     assert oracle.sparse_layers(R) == [2, 4, 5, 6]
@@ -408,8 +508,23 @@ def _mut_ratio_floor(L, sparsity):
     return k, L - k
 
 
+def _mut_block_no_diagonal(qbar, kbar, gamma):
+    nb, d = qbar.shape
+    keep = []
+    for I in range(nb):
+        z = (kbar[: I + 1] @ qbar[I]) / np.sqrt(d)
+        a = np.exp(z - z.max())
+        a = a / a.sum()
+        order = np.lexsort((np.arange(I + 1), -a))
+        hit = np.nonzero(np.cumsum(a[order]) >= gamma)[0]
+        n = int(hit[0]) + 1 if (gamma < 1 and len(hit)) else I + 1
+        keep.append(np.array(sorted(set(order[:n].tolist()) | {0}), dtype=np.int64))
+    return keep
+
+
 @pytest.mark.parametrize("name,mutant,pin", [
     ("budget_fixed_ratio", _mut_ratio_floor, test_budget_fixed_ratio_hand_cases),
+    ("block_select", _mut_block_no_diagonal, test_block_select_hand_case),
     ("head_scores", _mut_no_causal, lambda: test_score_zero_keys_closed_form(64, 16)),
     ("budget", _mut_budget_strict, lambda: test_budget_exhaustive_exact(0)),
     ("select", _mut_select_high_index_ties, test_select_zero_keys_keeps_the_prefix),
