@@ -196,6 +196,44 @@ def ratio_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
     return out
 
 
+def block_sparse_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
+    """Block sparsity stacked on the token selection at this workload's shapes: for a coverage
+    threshold tau (token budget) and a block coverage gamma, the share of causal key blocks kept,
+    the layer time and the speedup over dense."""
+    dev = Q.device
+    out = []
+    for tau in (cfg.tau, 0.5):
+        s = binding.shape(cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.q, tau, cfg.dtype)
+        C, NB = binding.capacity(cfg.L), binding.block_count(cfg.L)
+        sws = binding.workspace(binding.stage_workspace_bytes(s), dev)
+        s_h = torch.empty(cfg.Hq, cfg.L, dtype=torch.float32, device=dev)
+        s_l = torch.empty(cfg.L, dtype=torch.float32, device=dev)
+        kl = torch.zeros(2, dtype=torch.int32, device=dev)
+        idx = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
+        binding.score(s, Q, K, s_h, s_l, sws)
+        binding.budget(s, s_l, kl[0:1], kl[1:2], sws)
+        binding.select(s, s_h, kl[1:2], idx, None, sws)
+        Qh = torch.empty(cfg.Hq, C, cfg.d, dtype=Q.dtype, device=dev)
+        Kh, Vht = torch.empty_like(Qh), torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
+        binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht)
+        del sws, s_h, s_l, idx, Vht
+        Lp = int(kl[1])
+        nb = -(-Lp // 128)
+        blist = torch.empty(cfg.Hq, NB, NB, dtype=torch.int16, device=dev)
+        bcnt = torch.empty(cfg.Hq, NB, dtype=torch.int32, device=dev)
+        bws = binding.workspace(binding.block_select_workspace_bytes(s), dev)
+        lws = binding.workspace(binding.layer_block_sparse_workspace_bytes(s), dev)
+        Y = torch.empty_like(X)
+        for gamma in (0.9, 0.5):
+            binding.block_select(s, gamma, Qh, Kh, kl[1:2], blist, bcnt, bws)
+            kept = int(bcnt[:, :nb].sum()) / (cfg.Hq * nb * (nb + 1) / 2)
+            ms = timed(lambda: binding.layer_block_sparse(s, gamma, Q, K, V, X, Y, None, lws), steps, warmup, stream)
+            out.append({"tau": tau, "gamma": gamma, "L_keep": Lp, "kept_block_frac": round(kept, 4),
+                        "layer_ms": round(ms, 3), "speedup_vs_dense": round(dense_ms / ms, 3)})
+        del Qh, Kh, blist, bcnt, bws, lws, Y
+    return out
+
+
 VARLEN_LENGTHS = [32768, 24576, 16384, 16384, 8192, 8192, 4096, 4096]
 
 
@@ -249,6 +287,7 @@ def main():
     ap.add_argument("--workload", type=int, default=4, help="workload number (4 = L=128K headline)")
     ap.add_argument("--no-tau-sweep", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-block-sparse", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the short kernel sequence used for the rocprofv3 counter passes")
     args = ap.parse_args()
@@ -357,6 +396,9 @@ def main():
         out["supplementary_tau_sweep"] = tau_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1, stream)
         out["supplementary_fixed_ratio"] = ratio_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1,
                                                        stream)
+    if not args.no_block_sparse:
+        out["supplementary_block_sparse"] = block_sparse_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1,
+                                                               stream)
     if not args.no_varlen:
         del Qh, Kh, Vht, Oh, Ys, ws, sws
         out["supplementary_varlen"] = varlen_batch(max(2, args.steps // 2), 1, stream, dev)

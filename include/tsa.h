@@ -155,6 +155,45 @@ int tsa_layer_ratio(const tsa_shape* s, float sparsity, const void* Q, const voi
 int tsa_dense_attn_causal(const tsa_shape* s, const void* Q, const void* K, const void* V,
                           const void* X, void* Y, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- Block sparsity stacked on the token selection --------------------------------------------
+ * The compressed Q_hat, K_hat, V_hat are dense and contiguous, so a block-sparse attention can run
+ * on them after the token filter (notes, "Key findings"; article 3.2: token selection first, then
+ * block-sparse computation).  The pages give no block rule; this library's rule mirrors the
+ * coverage budget.  Blocks are 128 consecutive compressed rows; NB = tsa_block_count(L) blocks per
+ * head (at most 4096, i.e. L <= 524288: TSA_ERR_UNSUPPORTED otherwise).
+ *   pool   : qbar[h][b], kbar[h][b] = mean of block b's rows of Qh[h], Kh[h] (float64 sum in row
+ *            order, rounded once to float32);
+ *   select : for query block I, a_J = softmax over J <= I of <qbar_I, kbar_J> / sqrt(d) (float64);
+ *            keep the fewest heaviest J (ties: lower J) whose weights sum to >= gamma (all J when
+ *            gamma >= 1 or no prefix does), plus J = 0 and J = I;
+ *   attend : query row i of block I sees the keys j <= i of its kept blocks only.
+ * Lists: list [Hq][NB][NB] uint16, row (h, I) holds count[h][I] kept blocks ascending; count
+ * [Hq][NB] int32 (0 for blocks at or past L'). */
+
+/* Key blocks per head for length L (tsa_capacity(L) / 128). */
+int64_t tsa_block_count(int64_t L);
+/* Workspace of tsa_block_select and of tsa_layer_block_sparse.  tsa_block_select leaves the pooled
+ * means in its workspace: qbar [Hq][NB][d] float32 at byte 0, kbar at the next multiple of 256
+ * bytes after it. */
+size_t tsa_block_select_workspace_bytes(const tsa_shape* s);
+size_t tsa_layer_block_sparse_workspace_bytes(const tsa_shape* s);
+
+/* Pool the compressed Qh, Kh (layout of tsa_gather, L' from Lp_dev) and write the kept key blocks
+ * of every query block.  gamma >= 0 (NaN rejected). */
+int tsa_block_select(const tsa_shape* s, float gamma, const void* Qh, const void* Kh, const int32_t* Lp_dev,
+                     uint16_t* list, int32_t* count, void* ws, size_t ws_bytes, void* stream);
+
+/* tsa_attn_causal restricted to the kept key blocks (list, count from tsa_block_select).  With every
+ * block kept it computes exactly what tsa_attn_causal computes, bit for bit. */
+int tsa_attn_block_sparse(const tsa_shape* s, const void* Qh, const void* Kh, const void* Vht, const int32_t* Lp_dev,
+                          const uint16_t* list, const int32_t* count, void* Oh, void* stream);
+
+/* tsa_layer with block-sparse compressed attention: scoring, budget, selection and compression as
+ * in tsa_layer, then tsa_block_select and tsa_attn_block_sparse, then decompression and the
+ * residual.  Workspace: tsa_layer_block_sparse_workspace_bytes. */
+int tsa_layer_block_sparse(const tsa_shape* s, float gamma, const void* Q, const void* K, const void* V,
+                           const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Batches of sequences of different lengths (varlen) -------------------------------------
  * The keep count L' is data dependent, so the samples of a batch compress to different lengths
  * (notes, "Limitations", names this raggedness as a practical cost of batching).  A batch packs B

@@ -168,3 +168,25 @@ def test_varlen_capacity_and_validation():
     with pytest.raises(binding.TsaError) as e:                # valid batch, no workspace
         binding.layer_varlen(s, cu, p, p, p, None, p, stream=0)
     assert e.value.status == 5
+
+
+def test_block_sparse_host_rules():
+    assert binding.block_count(1) == 2 and binding.block_count(131072) == 1024
+    s = good()
+    assert binding.block_select_workspace_bytes(s) >= 2 * 32 * binding.block_count(4096) * 128 * 4
+    assert binding.layer_block_sparse_workspace_bytes(s) > binding.layer_workspace_bytes(s)
+    p = FakePtr(1 << 20)
+    for g in (-0.5, float("nan")):
+        with pytest.raises(binding.TsaError) as e:
+            binding.block_select(s, g, p, p, p, p, p, stream=0)
+        assert e.value.status == 1
+        with pytest.raises(binding.TsaError) as e:
+            binding.layer_block_sparse(s, g, p, p, p, None, p, stream=0)
+        assert e.value.status == 1
+    big = binding.shape(524289, 8, 8, 128, 16, 0.005, "bf16")       # more than 4096 key blocks
+    with pytest.raises(binding.TsaError) as e:
+        binding.attn_block_sparse(big, p, p, p, p, p, p, p, stream=0)
+    assert e.value.status == 7
+    with pytest.raises(binding.TsaError) as e:                       # no workspace
+        binding.block_select(s, 0.9, p, p, p, p, p, stream=0)
+    assert e.value.status == 5

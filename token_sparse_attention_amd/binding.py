@@ -44,10 +44,15 @@ _SIGS = {
     "tsa_attn_causal_varlen": [ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P],
     "tsa_layer_varlen": [ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_dense_attn_causal_varlen": [ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_block_select": [ctypes.c_float, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_attn_block_sparse": [_P, _P, _P, _P, _P, _P, _P, _P],
+    "tsa_layer_block_sparse": [ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
 }
+_SHAPE_WS = ("tsa_block_select_workspace_bytes", "tsa_layer_block_sparse_workspace_bytes")
 _VARLEN_WS = ("tsa_layer_varlen_workspace_bytes", "tsa_dense_varlen_workspace_bytes")
 EXPORTS = ["tsa_status_string", "tsa_check_args", "tsa_capacity", "tsa_stage_workspace_bytes",
-           "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SIGS, "tsa_varlen_capacity", *_VARLEN_WS]
+           "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SIGS, "tsa_varlen_capacity", *_VARLEN_WS,
+           "tsa_block_count", *_SHAPE_WS]
 
 
 def lib():
@@ -65,7 +70,9 @@ def lib():
         L.tsa_check_args.argtypes = [sp]
         L.tsa_capacity.restype = ctypes.c_int64
         L.tsa_capacity.argtypes = [ctypes.c_int64]
-        for n in ("tsa_stage_workspace_bytes", "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes"):
+        L.tsa_block_count.restype = ctypes.c_int64
+        L.tsa_block_count.argtypes = [ctypes.c_int64]
+        for n in ("tsa_stage_workspace_bytes", "tsa_layer_workspace_bytes", "tsa_dense_workspace_bytes", *_SHAPE_WS):
             getattr(L, n).restype = ctypes.c_size_t
             getattr(L, n).argtypes = [sp]
         for n, args in _SIGS.items():
@@ -241,3 +248,36 @@ def dense_attn_causal_varlen(s, cu_seqlens, Q, K, V, X, Y, ws=None, stream=None)
     _check("tsa_dense_attn_causal_varlen", lib().tsa_dense_attn_causal_varlen(
         ctypes.byref(s), B, ctypes.cast(arr, _P), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y), p, n,
         _stream(stream)))
+
+
+# -- block sparsity in the compressed space ---------------------------------------------------------
+
+def block_count(L):
+    return lib().tsa_block_count(int(L))
+
+
+def block_select_workspace_bytes(s):
+    return lib().tsa_block_select_workspace_bytes(ctypes.byref(s))
+
+
+def layer_block_sparse_workspace_bytes(s):
+    return lib().tsa_layer_block_sparse_workspace_bytes(ctypes.byref(s))
+
+
+def block_select(s, gamma, Qh, Kh, Lp_dev, blist, bcnt, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_block_select", lib().tsa_block_select(ctypes.byref(s), float(gamma), _ptr(Qh), _ptr(Kh), _ptr(Lp_dev),
+                                                      _ptr(blist), _ptr(bcnt), p, n, _stream(stream)))
+
+
+def attn_block_sparse(s, Qh, Kh, Vht, Lp_dev, blist, bcnt, Oh, stream=None):
+    _check("tsa_attn_block_sparse", lib().tsa_attn_block_sparse(ctypes.byref(s), _ptr(Qh), _ptr(Kh), _ptr(Vht),
+                                                                _ptr(Lp_dev), _ptr(blist), _ptr(bcnt), _ptr(Oh),
+                                                                _stream(stream)))
+
+
+def layer_block_sparse(s, gamma, Q, K, V, X, Y, kLp_dev=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check("tsa_layer_block_sparse", lib().tsa_layer_block_sparse(ctypes.byref(s), float(gamma), _ptr(Q), _ptr(K),
+                                                                  _ptr(V), _ptr(X), _ptr(Y), _ptr(kLp_dev), p, n,
+                                                                  _stream(stream)))

@@ -46,10 +46,18 @@ StageWs stage_layout(const tsa_shape* s) {
   return w;
 }
 
-// The layer workspace = stage workspace + every intermediate tensor of the layer.
+// Block sparsity: key blocks per head, pooled means and kept-block lists.
+int64_t block_count(const tsa_shape* s) { return tsa_capacity(s->L) / kBlock; }
+size_t pooled_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * s->d * sizeof(float); }
+size_t list_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * block_count(s) * sizeof(uint16_t); }
+size_t count_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * sizeof(int32_t); }
+
+// The layer workspace = stage workspace + every intermediate tensor of the layer (+ the block
+// lists of the block-sparse variant).
 struct LayerWs {
   StageWs st;
   size_t s_h, s_l, idx, inv, Qh, Kh, Vht, Oh, total;
+  size_t qbar, kbar, blist, bcnt, total_bs;
 };
 
 LayerWs layer_layout(const tsa_shape* s) {
@@ -69,6 +77,11 @@ LayerWs layer_layout(const tsa_shape* s) {
   w.Vht = take(comp);
   w.Oh = take(comp);
   w.total = o;
+  w.qbar = take(pooled_bytes(s));
+  w.kbar = take(pooled_bytes(s));
+  w.blist = take(list_bytes(s));
+  w.bcnt = take(count_bytes(s));
+  w.total_bs = o;
   return w;
 }
 
@@ -187,13 +200,14 @@ VarlenWs varlen_layout(const tsa_shape* s, int32_t B, const int64_t* cu) {
 // (k = round(sparsity * L)) in place of the coverage budget; s_l is then not needed.
 int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* Q, const void* K,
               const void* V, const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes,
-              void* stream) {
+              void* stream, bool block_sparse = false, float gamma = 1.f) {
   TSA_TRY(tsa_check_args(s));
   TSA_TRY(need_ptrs({Q, K, V, Y}));
   TSA_TRY(opt_ptrs({X}));
   if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
+  if (block_sparse && block_count(s) > kMaxKeyBlocks) return TSA_ERR_UNSUPPORTED;
   const LayerWs w = layer_layout(s);
-  TSA_TRY(check_ws(ws, ws_bytes, w.total));
+  TSA_TRY(check_ws(ws, ws_bytes, block_sparse ? w.total_bs : w.total));
   hipStream_t st = stream_of(stream);
   const StageWs& g = w.st;
   const int64_t C = tsa_capacity(s->L);
@@ -223,9 +237,19 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   if (e == hipSuccess)
     e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C, at<void>(ws, w.Qh),
                       at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
-  if (e == hipSuccess)
+  if (block_sparse) {
+    if (e == hipSuccess)
+      e = launch_block_select(s->dtype, s->d, at<void>(ws, w.Qh), at<void>(ws, w.Kh), kLp + 1, C, s->Hq, (double)gamma,
+                              at<float>(ws, w.qbar), at<float>(ws, w.kbar), at<uint16_t>(ws, w.blist),
+                              at<int32_t>(ws, w.bcnt), st);
+    if (e == hipSuccess)
+      e = launch_attention_block_sparse(s->dtype, s->d, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
+                                        kLp + 1, s->L, s->Hq, s->Hkv, C, at<uint16_t>(ws, w.blist),
+                                        at<int32_t>(ws, w.bcnt), at<void>(ws, w.Oh), st);
+  } else if (e == hipSuccess) {
     e = launch_attention(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
                          kLp + 1, s->L, s->Hq, s->Hkv, C, nullptr, at<void>(ws, w.Oh), st);
+  }
   if (e == hipSuccess)
     e = launch_scatter(s->dtype, s->d, at<void>(ws, w.Oh), idx, inv, kLp + 1, X, Y, s->L, s->Hq, C, st);
   return hip_status(e);
@@ -500,6 +524,46 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
                        X ? static_cast<const char*>(X) + row : nullptr, static_cast<char*>(Y) + row, Lb, s->Hq, Cb, st);
   }
   return hip_status(e);
+}
+
+int64_t tsa_block_count(int64_t L) { return tsa_capacity(L) / kBlock; }
+
+size_t tsa_block_select_workspace_bytes(const tsa_shape* s) {
+  return tsa_check_args(s) == TSA_OK ? 2 * up(pooled_bytes(s)) : 0;
+}
+
+size_t tsa_layer_block_sparse_workspace_bytes(const tsa_shape* s) {
+  return tsa_check_args(s) == TSA_OK ? layer_layout(s).total_bs : 0;
+}
+
+int tsa_block_select(const tsa_shape* s, float gamma, const void* Qh, const void* Kh, const int32_t* Lp_dev,
+                     uint16_t* list, int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  if (!(gamma >= 0.f)) return TSA_ERR_ARG;
+  TSA_TRY(need_ptrs({Qh, Kh, list, count}));
+  TSA_TRY(need_int_ptrs({Lp_dev}));
+  if (block_count(s) > kMaxKeyBlocks) return TSA_ERR_UNSUPPORTED;
+  TSA_TRY(check_ws(ws, ws_bytes, tsa_block_select_workspace_bytes(s)));
+  float* qbar = at<float>(ws, 0);
+  float* kbar = at<float>(ws, up(pooled_bytes(s)));
+  return hip_status(launch_block_select(s->dtype, s->d, Qh, Kh, Lp_dev, tsa_capacity(s->L), s->Hq, (double)gamma,
+                                        qbar, kbar, list, count, stream_of(stream)));
+}
+
+int tsa_attn_block_sparse(const tsa_shape* s, const void* Qh, const void* Kh, const void* Vht, const int32_t* Lp_dev,
+                          const uint16_t* list, const int32_t* count, void* Oh, void* stream) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Qh, Kh, Vht, Oh, list, count}));
+  TSA_TRY(need_int_ptrs({Lp_dev}));
+  if (block_count(s) > kMaxKeyBlocks) return TSA_ERR_UNSUPPORTED;
+  return hip_status(launch_attention_block_sparse(s->dtype, s->d, Qh, Kh, Vht, Lp_dev, s->L, s->Hq, s->Hkv,
+                                                  tsa_capacity(s->L), list, count, Oh, stream_of(stream)));
+}
+
+int tsa_layer_block_sparse(const tsa_shape* s, float gamma, const void* Q, const void* K, const void* V,
+                           const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream) {
+  if (!(gamma >= 0.f)) return TSA_ERR_ARG;
+  return run_layer(s, false, 0.f, Q, K, V, X, Y, kLp_dev, ws, ws_bytes, stream, true, gamma);
 }
 
 }  // extern "C"

@@ -53,6 +53,10 @@ struct AttnArgs {
   int Hq, Hkv;
   float scale;
   int nseg;
+  // block-sparse variant (one compressed sequence): ascending kept key blocks of every query block
+  const uint16_t* blist;  // [Hq][nbmax][nbmax]
+  const int32_t* bcnt;    // [Hq][nbmax]
+  int nbmax;
   AttnSeg seg[kMaxSeg];
 };
 
@@ -105,7 +109,7 @@ __host__ __device__ __forceinline__ void dma_1k(const void* base, uint32_t bytes
 #endif
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KS = D / 16;            // K-steps of 16 over the head dim (score product)
@@ -119,6 +123,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int NS = 2 * KS, NV = 4 * DT, PF = 3;
   // LDS: K slots 0,1 then V slots 0,1
   __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * VTILE];
+  __shared__ uint16_t klist[SPARSE ? kMaxKeyBlocks : 1];
 
   int h, mb;
   const AttnSeg& sg = block_coords(a, h, mb);
@@ -150,7 +155,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       qf[s] = qi < Lp ? *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s) : bf16x8_t{};
   }
   const int kend = m0 + BM < Lp ? m0 + BM : Lp;
-  const int nkb = (kend + BN - 1) / BN;
+  // key tiles walked: all up to the diagonal, or (block sparse) the two tiles of every listed key
+  // block, the last listed block being the diagonal one (query block mb = key block mb)
+  int nkb = (kend + BN - 1) / BN;
+  if constexpr (SPARSE) {
+    const size_t row = (size_t)h * a.nbmax + mb;
+    const int nlist = a.bcnt[row];
+    for (int i = threadIdx.x; i < nlist; i += 256) klist[i] = a.blist[row * a.nbmax + i];
+    nkb = 2 * (nlist - 1) + (kend - m0 + BN - 1) / BN;
+    __syncthreads();
+  }
+  // tile t of the walk -> key tile index
+  auto ktile = [&](int t) -> int {
+    if constexpr (SPARSE) return 2 * __builtin_amdgcn_readfirstlane((int)klist[t >> 1]) + (t & 1);
+    else return t;
+  };
 
   // Tile layouts.  K: LDS row m holds key perm(m) (bits 2 and 3 of the key swapped), 16-byte chunk
   // c of a row sits in slot c ^ kswz(m).  V^T: row = head-dim index, chunk c (keys 8c..8c+7) in
@@ -204,9 +223,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  dma_k(0, 0);
-  dma_v(0, 0);
-  if (nkb > 1) dma_k(1, 1);
+  dma_k(ktile(0), 0);
+  dma_v(ktile(0), 0);
+  if (nkb > 1) dma_k(ktile(1), 1);
   TSA_WAIT_VMEM();
   __syncthreads();
   f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
@@ -219,9 +238,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   auto tile = [&](int kb, int P) {     // P = kb & 1, a literal at both call sites
     const char* kslot = smem + (P ^ 1) * KTILE;
     const char* vslot = smem + 2 * KTILE + P * VTILE;
-    if (kb + 2 < nkb) dma_k(kb + 2, P);
-    if (kb + 1 < nkb) dma_v(kb + 1, P ^ 1);
-    const int key0 = kb * BN, nval = Lp - key0;
+    if (kb + 2 < nkb) dma_k(ktile(kb + 2), P);
+    if (kb + 1 < nkb) dma_v(ktile(kb + 1), P ^ 1);
+    const int key0 = ktile(kb) * BN, nval = Lp - key0;
     if (nval < BN) {                    // last tile: zero the V^T columns at and beyond L'
       for (int e = tid; e < D * (BN - nval); e += 256) {
         const int r = e / (BN - nval), col = nval + e % (BN - nval);
@@ -337,11 +356,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 // ------------------------------------------------------------------------------------------------
 // f32, vector ALU
 // ------------------------------------------------------------------------------------------------
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int TPR = 4, BM = 256 / TPR, BN = 32, DPT = D / TPR;
   __shared__ float smK[BN][D + 1];
   __shared__ float smV[BN][D + 1];
+  __shared__ uint16_t klist[SPARSE ? kMaxKeyBlocks : 1];
   int h, mb;
   const AttnSeg& sg = block_coords(a, h, mb);
   const int64_t Lp = DENSE ? sg.L : (int64_t)sg.Lp[0];
@@ -370,7 +390,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
   float m_run = -INFINITY, l_run = 0.f;
   const int64_t kend = (m0 + BM < Lp ? m0 + BM : Lp);
-  for (int64_t key0 = 0; key0 < kend; key0 += BN) {
+  // key ranges walked: [0, kend), or (block sparse) every listed key block of this rows' query block
+  int nrange = 1;
+  if constexpr (SPARSE) {
+    const size_t row = (size_t)h * a.nbmax + m0 / kBlock;
+    nrange = a.bcnt[row];
+    for (int i = threadIdx.x; i < nrange; i += 256) klist[i] = a.blist[row * a.nbmax + i];
+    __syncthreads();
+  }
+  for (int rg = 0; rg < nrange; ++rg) {
+  const int64_t kbeg = SPARSE ? (int64_t)klist[rg] * kBlock : 0;
+  const int64_t kstop = SPARSE ? (kbeg + kBlock < kend ? kbeg + kBlock : kend) : kend;
+  for (int64_t key0 = kbeg; key0 < kstop; key0 += BN) {
     __syncthreads();
     for (int e = tid; e < BN * D; e += 256) {
       const int r = e / D, c = e % D;
@@ -407,6 +438,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       for (int u = 0; u < DPT; ++u) acc[u] = fmaf(p, smV[j][part + TPR * u], acc[u]);
     }
   }
+  }
   if (qi >= Lp) return;
   const float inv_l = 1.f / l_run;
   float* Op = static_cast<float*>(a.O);
@@ -420,12 +452,12 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool DENSE>
+template <int D, bool DENSE, bool SPARSE = false>
 static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st) {
   if (dtype == 1)
-    attn_bf16_kernel<D, DENSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
+    attn_bf16_kernel<D, DENSE, SPARSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
   else
-    attn_f32_kernel<D, DENSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
+    attn_f32_kernel<D, DENSE, SPARSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -453,6 +485,20 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const void* Kh, const void* Vht,
+                                         const int32_t* Lp_dev, int64_t L, int Hq, int Hkv, int64_t C,
+                                         const uint16_t* list, const int32_t* count, void* Oh, hipStream_t st) {
+  const int bm = dtype == 1 ? 128 : 64;
+  AttnArgs a{};
+  a.Q = Qh; a.K = Kh; a.Vt = Vht; a.X = nullptr; a.O = Oh;
+  a.Hq = Hq; a.Hkv = Hkv; a.scale = (float)(1.0 / sqrt((double)d));
+  a.blist = list; a.bcnt = count; a.nbmax = (int)(C / kBlock);
+  a.nseg = 1;
+  a.seg[0] = AttnSeg{0, 0, L, C, Lp_dev, 0, (int)((L + bm - 1) / bm)};
+  const int nblocks = a.seg[0].nmb * Hq;
+  return d == 128 ? run_attn<128, false, true>(dtype, a, nblocks, st) : run_attn<64, false, true>(dtype, a, nblocks, st);
 }
 
 hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const void* K,

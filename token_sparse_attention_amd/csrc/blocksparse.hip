@@ -1,0 +1,216 @@
+// Block sparsity stacked on the token selection: inside the compressed space (Q_hat, K_hat, V_hat
+// of one head are dense and contiguous) the causal attention is restricted to a per-query-block set
+// of key blocks (papernotes.org reading notes, "Key findings": the token filter composes with a
+// block-sparse kernel; bxzpzcl.cn article, section 3.2: token selection first, then block-sparse
+// computation).  The pages give no block rule of their own; this one mirrors the coverage budget:
+//
+//   pool   : the rows of every block of kBlock compressed rows are averaged (float64 sum in row
+//            order, one division, rounded once to float32) into qbar, kbar [Hq][NB][d];
+//   select : query block I weighs its causal key blocks J <= I by a_J = softmax_J(<qbar_I, kbar_J>
+//            / sqrt(d)) (float64) and keeps the fewest heaviest (ties: lower J) whose weight reaches
+//            gamma (all of them when gamma >= 1 or no prefix does), plus J = 0 and J = I.  The kept
+//            blocks are listed ascending: list [Hq][NB][NB] (uint16), count [Hq][NB].
+//
+// The attention kernel then walks only the listed blocks' key tiles (attention.hip).
+#include "kern_common.h"
+#include "tsa_internal.h"
+
+namespace tsa {
+
+constexpr int kSortMax = kMaxKeyBlocks;       // candidates sorted in LDS per query block
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ Qh, const T* __restrict__ Kh,
+                                                         const int32_t* __restrict__ Lp_dev, int64_t C, int nbmax,
+                                                         float* __restrict__ qbar, float* __restrict__ kbar) {
+  const int b = blockIdx.x, h = blockIdx.y;
+  const int64_t Lp = Lp_dev[0];
+  const int64_t r0 = (int64_t)b * kBlock;
+  if (r0 >= Lp || threadIdx.x >= 2 * D) return;
+  const int64_t r1 = r0 + kBlock < Lp ? r0 + kBlock : Lp;
+  const bool isk = threadIdx.x >= D;
+  const int c = threadIdx.x % D;
+  const T* src = (isk ? Kh : Qh) + ((size_t)h * C) * D + c;
+  double acc = 0.0;
+  int64_t r = r0;
+  for (; r + 8 <= r1; r += 8) {             // loads first, then the adds in row order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = to_f32(src[(size_t)(r + u) * D]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += (double)v[u];
+  }
+  for (; r < r1; ++r) acc += (double)to_f32(src[(size_t)r * D]);
+  (isk ? kbar : qbar)[((size_t)h * nbmax + b) * D + c] = (float)(acc / (double)(r1 - r0));
+}
+
+// "x comes before y": heavier first, then lower block index
+__device__ __forceinline__ bool before(double ax, int jx, double ay, int jy) {
+  return ax > ay || (ax == ay && jx < jy);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void block_select_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                           const int32_t* __restrict__ Lp_dev, int nbmax, double gamma,
+                                                           uint16_t* __restrict__ list, int32_t* __restrict__ count) {
+  __shared__ double av[kSortMax];
+  __shared__ uint16_t jv[kSortMax];
+  __shared__ float qb[D];
+  __shared__ double red[4];
+  __shared__ uint32_t kept[kSortMax / 32];
+  __shared__ uint32_t wbase[kSortMax / 32];
+  __shared__ double tot[256];
+  __shared__ int cut;
+  const int I = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t Lp = Lp_dev[0];
+  const int nb = (int)((Lp + kBlock - 1) / kBlock);
+  if (I >= nb) {
+    if (tid == 0) count[(size_t)h * nbmax + I] = 0;
+    return;
+  }
+  const int n = I + 1;
+  int P2 = 1;
+  while (P2 < n) P2 <<= 1;
+  for (int c = tid; c < D; c += 256) qb[c] = qbar[((size_t)h * nbmax + I) * D + c];
+  for (int i = tid; i < kSortMax / 32; i += 256) kept[i] = 0;
+  if (tid == 0) cut = n - 1;
+  __syncthreads();
+
+  // logits, max
+  const double rsd = sqrt((double)D);
+  double mx = -INFINITY;
+  for (int J = tid; J < n; J += 256) {
+    const float* kr = kbar + ((size_t)h * nbmax + J) * D;
+    double z = 0.0;
+#pragma unroll 8
+    for (int c = 0; c < D; ++c) z += (double)qb[c] * (double)kr[c];
+    z /= rsd;
+    av[J] = z;
+    mx = fmax(mx, z);
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+  __syncthreads();
+  // weights
+  double sum = 0.0;
+  for (int J = tid; J < n; J += 256) {
+    const double e = exp(av[J] - mx);
+    av[J] = e;
+    sum += e;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  sum = (red[0] + red[1]) + (red[2] + red[3]);
+  for (int J = tid; J < P2; J += 256) {
+    if (J < n) {
+      av[J] = av[J] / sum;
+      jv[J] = (uint16_t)J;
+    } else {
+      av[J] = -1.0;                          // padding sorts last
+      jv[J] = 0xFFFF;
+    }
+  }
+  __syncthreads();
+  // bitonic sort of P2 (weight, block) pairs into "before" order
+  for (int k = 2; k <= P2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P2; i += 256) {
+        const int p = i ^ j;
+        if (p > i) {
+          const bool up = (i & k) == 0;        // this run is sorted in "before" order
+          const double a0 = av[i], a1 = av[p];
+          const int j0 = jv[i], j1 = jv[p];
+          const bool swap = up ? before(a1, j1, a0, j0) : before(a0, j0, a1, j1);
+          if (swap) {
+            av[i] = a1; av[p] = a0;
+            jv[i] = (uint16_t)j1; jv[p] = (uint16_t)j0;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // cumulative weight in sorted order: contiguous chunks per thread, chunk totals scanned in
+  // thread order, then each thread finds its first position reaching gamma
+  if (gamma < 1.0) {
+    const int per = (n + 255) / 256, lo = tid * per, hi = lo + per < n ? lo + per : n;
+    double part = 0.0;
+    for (int i = lo; i < hi; ++i) part += av[i];
+    // exclusive scan of the 256 chunk totals in thread order
+    tot[tid] = part;
+    __syncthreads();
+    if (tid == 0) {
+      double run = 0.0;
+      for (int t = 0; t < 256; ++t) {
+        const double v = tot[t];
+        tot[t] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    double cum = tot[tid];
+    for (int i = lo; i < hi; ++i) {
+      cum += av[i];
+      if (cum >= gamma) {
+        atomicMin(&cut, i);
+        break;
+      }
+    }
+    __syncthreads();
+  }
+  const int p = cut;
+  for (int i = tid; i <= p; i += 256) atomicOr(&kept[jv[i] >> 5], 1u << (jv[i] & 31));
+  if (tid == 0) {
+    atomicOr(&kept[0], 1u);
+    atomicOr(&kept[I >> 5], 1u << (I & 31));
+  }
+  __syncthreads();
+  // ascending list: exclusive popcount scan over the bitmap words
+  const int nw = (n + 31) / 32;
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int i = 0; i < nw; ++i) {
+      wbase[i] = run;
+      run += __popc(kept[i]);
+    }
+    count[(size_t)h * nbmax + I] = (int32_t)run;
+  }
+  __syncthreads();
+  uint16_t* out = list + ((size_t)h * nbmax + I) * nbmax;
+  for (int i = tid; i < nw * 32 && i < n; i += 256) {
+    const uint32_t word = kept[i >> 5];
+    if ((word >> (i & 31)) & 1u) out[wbase[i >> 5] + __popc(word & ((1u << (i & 31)) - 1u))] = (uint16_t)i;
+  }
+}
+
+hipError_t launch_block_select(int dtype, int d, const void* Qh, const void* Kh, const int32_t* Lp_dev, int64_t C,
+                               int Hq, double gamma, float* qbar, float* kbar, uint16_t* list, int32_t* count,
+                               hipStream_t st) {
+  const int nbmax = (int)(C / kBlock);
+  const dim3 grid((unsigned)nbmax, (unsigned)Hq);
+  if (dtype == 1) {
+    if (d == 128)
+      block_pool_kernel<uint16_t, 128><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(Qh),
+                                                             static_cast<const uint16_t*>(Kh), Lp_dev, C, nbmax, qbar, kbar);
+    else
+      block_pool_kernel<uint16_t, 64><<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(Qh),
+                                                            static_cast<const uint16_t*>(Kh), Lp_dev, C, nbmax, qbar, kbar);
+  } else {
+    if (d == 128)
+      block_pool_kernel<float, 128><<<grid, 256, 0, st>>>(static_cast<const float*>(Qh), static_cast<const float*>(Kh),
+                                                          Lp_dev, C, nbmax, qbar, kbar);
+    else
+      block_pool_kernel<float, 64><<<grid, 256, 0, st>>>(static_cast<const float*>(Qh), static_cast<const float*>(Kh),
+                                                         Lp_dev, C, nbmax, qbar, kbar);
+  }
+  if (d == 128)
+    block_select_kernel<128><<<grid, 256, 0, st>>>(qbar, kbar, Lp_dev, nbmax, gamma, list, count);
+  else
+    block_select_kernel<64><<<grid, 256, 0, st>>>(qbar, kbar, Lp_dev, nbmax, gamma, list, count);
+  return hipGetLastError();
+}
+
+}  // namespace tsa

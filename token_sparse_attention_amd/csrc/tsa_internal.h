@@ -54,6 +54,17 @@ hipError_t launch_scatter(int dtype, int d, const void* Oh, const int32_t* idx, 
                           const int32_t* Lp_dev, const void* X, void* Y, int64_t L, int Hq,
                           int64_t C, hipStream_t st);
 
+// ---- blocksparse.hip ----------------------------------------------------------------------------
+// Blocks of kBlock compressed rows (= the bf16 attention kernel's query rows per workgroup); at most
+// kMaxKeyBlocks blocks per head (capacity <= kBlock * kMaxKeyBlocks rows).
+constexpr int kBlock = 128;
+constexpr int kMaxKeyBlocks = 4096;
+// Pools Qh/Kh [Hq][C][d] into qbar/kbar [Hq][C/kBlock][d] (float32) and writes the kept key blocks
+// of every query block: list [Hq][NB][NB] ascending, count [Hq][NB] (0 past the last block).
+hipError_t launch_block_select(int dtype, int d, const void* Qh, const void* Kh, const int32_t* Lp_dev, int64_t C,
+                               int Hq, double gamma, float* qbar, float* kbar, uint16_t* list, int32_t* count,
+                               hipStream_t st);
+
 // ---- attention.hip ------------------------------------------------------------------------------
 // Compressed (dense == false): Qh/Kh [Hq][C][d], Vht [Hq][d][C], L' from Lp_dev, output Oh.
 // Dense (dense == true): Q [L][Hq][d], K [L][Hkv][d], Vt [Hkv][d][C] (C >= L), output
@@ -73,5 +84,10 @@ struct AttnSeqDesc {
 hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, const void* K, const void* Vt,
                                    int nseq, const AttnSeqDesc* seqs, int Hq, int Hkv, const void* X, void* O,
                                    hipStream_t st);
+// Compressed attention restricted to the listed key blocks of every query block (launch_block_select's
+// list and count, NB = C / kBlock).
+hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const void* Kh, const void* Vht,
+                                         const int32_t* Lp_dev, int64_t L, int Hq, int Hkv, int64_t C,
+                                         const uint16_t* list, const int32_t* count, void* Oh, hipStream_t st);
 
 }  // namespace tsa
