@@ -312,6 +312,21 @@ def test_layer_end_to_end(case):
     Xc = case.d["X"].clone()
     binding.layer(case.s, case.d["Q"], case.d["K"], case.d["V"], Xc, Xc, None, ws)
     assert torch.equal(Xc, Y)
+    # the layer (bf16: queries read through idx and Y written by the attention itself) is bitwise
+    # the stage-by-stage composition gather -> attention -> scatter
+    Lp_t = case.lp_tensor(Lp)
+    it, iv = case.idx_tensor(idx)
+    Qh, Kh, Vht = case.gpu_gather(idx)
+    Oh = case.empty(cfg.Hq, case.C, cfg.d)
+    binding.attn_causal(case.s, Qh, Kh, Vht, Lp_t, Oh)
+    Ys = case.empty(cfg.L, cfg.Hq, cfg.d)
+    binding.scatter_residual(case.s, Oh, it, iv, Lp_t, case.d["X"], Ys)
+    assert torch.equal(Ys, Y)
+    # without X: the pure decompression, unselected rows +0.0
+    Y0 = case.empty(cfg.L, cfg.Hq, cfg.d).fill_(7.0)
+    binding.layer(case.s, case.d["Q"], case.d["K"], case.d["V"], None, Y0, None, ws)
+    binding.scatter_residual(case.s, Oh, it, iv, Lp_t, None, Ys)
+    assert torch.equal(Y0, Ys) and not torch.signbit(Y0[Y0 == 0]).any()
 
 
 def test_dense_attention(case):

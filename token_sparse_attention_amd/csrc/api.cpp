@@ -234,9 +234,21 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   if (e == hipSuccess)
     e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
                       at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
+  // bf16 without block sparsity: the attention reads the queries through idx and writes Y itself
+  // (gather of the queries and decompression folded into it); the result is bitwise the same
+  const bool fused = s->dtype == TSA_BF16 && !block_sparse;
   if (e == hipSuccess)
-    e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C, at<void>(ws, w.Qh),
-                      at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
+    e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C,
+                      fused ? nullptr : at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
+  if (fused) {
+    if (e == hipSuccess) e = launch_fill_unselected(s->dtype, s->d, inv, X, Y, s->L, s->Hq, st);
+    if (e == hipSuccess) {
+      const AttnSeqDesc one{0, 0, s->L, C, kLp + 1, idx};
+      e = launch_attention_varlen(s->dtype, s->d, false, Q, at<void>(ws, w.Kh), at<void>(ws, w.Vht), 1, &one, s->Hq,
+                                  s->Hkv, X, Y, st, true);
+    }
+    return hip_status(e);
+  }
   if (block_sparse) {
     if (e == hipSuccess)
       e = launch_block_select(s->dtype, s->d, at<void>(ws, w.Qh), at<void>(ws, w.Kh), kLp + 1, C, s->Hq, (double)gamma,
@@ -433,7 +445,7 @@ int tsa_attn_causal_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seql
   std::vector<int64_t> P(B + 1, 0);
   for (int32_t b = 0; b < B; ++b) P[b + 1] = P[b] + tsa_capacity(cu_seqlens[b + 1] - cu_seqlens[b]);
   for (int32_t b : longest_first(B, cu_seqlens))
-    seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], Lp_dev + b});
+    seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], Lp_dev + b, nullptr});
   return hip_status(launch_attention_varlen(s->dtype, s->d, false, Qh, Kh, Vht, B, seqs.data(), s->Hq, s->Hkv,
                                             nullptr, Oh, stream_of(stream)));
 }
@@ -457,7 +469,7 @@ int tsa_dense_attn_causal_varlen(const tsa_shape* s, int32_t B, const int64_t* c
                            Lb, s->Hkv, P[b + 1] - P[b], static_cast<char*>(ws) + (size_t)P[b] * s->Hkv * s->d * eb, st);
   }
   for (int32_t b : longest_first(B, cu_seqlens))
-    seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], nullptr});
+    seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], nullptr, nullptr});
   if (e == hipSuccess)
     e = launch_attention_varlen(s->dtype, s->d, true, Q, K, ws, B, seqs.data(), s->Hq, s->Hkv, X, Y, st);
   return hip_status(e);
@@ -476,6 +488,7 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
   const StageWs& g = w.st;
   const size_t eb = elem_bytes(s->dtype), Hq = s->Hq, Hkv = s->Hkv, d = s->d;
   int32_t* kLp = at<int32_t>(ws, w.kLp);
+  const bool fused = s->dtype == TSA_BF16;
   std::vector<int64_t> P(B + 1, 0);
   for (int32_t b = 0; b < B; ++b) P[b + 1] = P[b] + tsa_capacity(cu_seqlens[b + 1] - cu_seqlens[b]);
   auto tok = [&](const void* base, size_t heads, int32_t b) {
@@ -505,18 +518,26 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
                         at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
     if (e == hipSuccess)
       e = launch_gather(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), tok(V, Hkv, b), idx, kl + 1, Lb, s->Hq,
-                        s->Hkv, Cb, comp(w.Qh, b), comp(w.Kh, b), comp(w.Vht, b), st);
+                        s->Hkv, Cb, fused ? nullptr : comp(w.Qh, b), comp(w.Kh, b), comp(w.Vht, b), st);
+    if (fused && e == hipSuccess)
+      e = launch_fill_unselected(s->dtype, s->d, inv, X ? tok(X, Hq, b) : nullptr,
+                                 static_cast<char*>(Y) + (size_t)cu_seqlens[b] * Hq * d * eb, Lb, s->Hq, st);
   }
-  // stage 4b: one launch over every sample's ragged L'_b
+  // stage 4b: one launch over every sample's ragged L'_b (fused: stage 5 in its epilogue)
   if (e == hipSuccess) {
     std::vector<AttnSeqDesc> seqs;
     for (int32_t b : longest_first(B, cu_seqlens))
-      seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], kLp + 2 * b + 1});
-    e = launch_attention_varlen(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
-                                B, seqs.data(), s->Hq, s->Hkv, nullptr, at<void>(ws, w.Oh), st);
+      seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], kLp + 2 * b + 1,
+                      at<int32_t>(ws, w.idx) + Hq * (size_t)P[b]});
+    if (fused)
+      e = launch_attention_varlen(s->dtype, s->d, false, Q, at<void>(ws, w.Kh), at<void>(ws, w.Vht), B, seqs.data(),
+                                  s->Hq, s->Hkv, X, Y, st, true);
+    else
+      e = launch_attention_varlen(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
+                                  B, seqs.data(), s->Hq, s->Hkv, nullptr, at<void>(ws, w.Oh), st);
   }
   // stage 5 sample by sample
-  for (int32_t b = 0; b < B && e == hipSuccess; ++b) {
+  for (int32_t b = 0; b < B && e == hipSuccess && !fused; ++b) {
     const int64_t Lb = cu_seqlens[b + 1] - cu_seqlens[b], Cb = P[b + 1] - P[b];
     const size_t row = (size_t)cu_seqlens[b] * Hq * d * eb;
     e = launch_scatter(s->dtype, s->d, comp(w.Oh, b), at<int32_t>(ws, w.idx) + Hq * (size_t)P[b],

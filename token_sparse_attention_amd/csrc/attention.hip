@@ -37,13 +37,17 @@ struct AttnSeg {
   int64_t L;            // dense: sequence length
   int64_t C;            // capacity of the sequence's region (multiple of 256, >= L)
   const int32_t* Lp;    // compressed: device keep count L'
+  const int32_t* idx;   // fused compressed: the sequence's selection [Hq][L] (ascending tokens)
   int32_t blk0;         // first block of the sequence in the grid
   int32_t nmb;          // query blocks per head
 };
 
 // Compressed: the region of sequence s in Qh, Kh, Oh is [Hq][C][d] and in Vht [Hq][d][C], starting
 // at element Hq * d * cap_off.  Dense: Q, X, Y [tokens][Hq][d], K [tokens][Hkv][d] from token
-// tok_off on; Vt [Hkv][d][C] (V transposed) from element Hkv * d * cap_off on.
+// tok_off on; Vt [Hkv][d][C] (V transposed) from element Hkv * d * cap_off on.  Fused compressed
+// (gather of the queries and decompression folded in): Kh, Vht as compressed; query row i of head h
+// is Q[tok_off + idx[h][i]][h] and its output goes to Y at that same row, plus X when given, after
+// rounding to the storage type as the separate decompression would.
 struct AttnArgs {
   const void* Q;
   const void* K;
@@ -109,7 +113,7 @@ __host__ __device__ __forceinline__ void dma_1k(const void* base, uint32_t bytes
 #endif
 }
 
-template <int D, bool DENSE, bool SPARSE>
+template <int D, bool DENSE, bool SPARSE, bool FUSED>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   constexpr int BM = 128, BN = 64;
   constexpr int KS = D / 16;            // K-steps of 16 over the head dim (score product)
@@ -135,11 +139,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = h / (a.Hq / a.Hkv);
   const int64_t C = sg.C;
-  const uint32_t q_rs = DENSE ? a.Hq * D * 2 : D * 2;
+  const uint32_t q_rs = (DENSE || FUSED) ? a.Hq * D * 2 : D * 2;
   const uint32_t k_rs = DENSE ? a.Hkv * D * 2 : D * 2;
   const uint32_t v_rs = (uint32_t)C * 2;
   // element offsets of this (sequence, head) in Q/O, K and V^T
-  const size_t qo_off = DENSE ? ((size_t)sg.tok_off * a.Hq + h) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
+  const size_t qo_off = (DENSE || FUSED) ? ((size_t)sg.tok_off * a.Hq + h) * D
+                                         : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
   const size_t k_off = DENSE ? ((size_t)sg.tok_off * a.Hkv + g) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
   const size_t v_off = (size_t)sg.cap_off * (DENSE ? a.Hkv : a.Hq) * D + (size_t)(DENSE ? g : h) * D * C;
   const char* qbase = static_cast<const char*>(a.Q) + qo_off * 2;
@@ -147,9 +152,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const char* vbase = static_cast<const char*>(a.Vt) + v_off * 2;
 
   const int qi = m0 + 32 * w + ln;      // this lane's query row
+  // its row in Q / X / Y: qi itself, or (fused) the token it stands for
+  const int64_t qrow_i = FUSED ? (qi < Lp ? (int64_t)sg.idx[(size_t)h * sg.L + qi] : 0) : qi;
   bf16x8_t qf[KS];
   {
-    const char* qrow = qbase + (size_t)qi * q_rs + (D / 2) * hf * 2;
+    const char* qrow = qbase + (size_t)qrow_i * q_rs + (D / 2) * hf * 2;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
       qf[s] = qi < Lp ? *reinterpret_cast<const bf16x8_t*>(qrow + 16 * s) : bf16x8_t{};
@@ -327,9 +334,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   if (qi >= Lp) return;
   const float inv_l = 1.f / l_tot;
-  uint16_t* orow = reinterpret_cast<uint16_t*>(static_cast<char*>(a.O) + qo_off * 2 + (size_t)qi * q_rs);
-  const uint16_t* xrow = DENSE && a.X
-      ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.X) + qo_off * 2 + (size_t)qi * q_rs)
+  uint16_t* orow = reinterpret_cast<uint16_t*>(static_cast<char*>(a.O) + qo_off * 2 + (size_t)qrow_i * q_rs);
+  const uint16_t* xrow = (DENSE || FUSED) && a.X
+      ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.X) + qo_off * 2 + (size_t)qrow_i * q_rs)
       : nullptr;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -339,6 +346,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
       float v[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) v[x] = o[dt][4 * rq + x] * inv_l;
+      if (FUSED) {                      // the stored O_hat value, as decompression would read it
+#pragma unroll
+        for (int x = 0; x < 4; ++x) v[x] = bf16_to_f32(f32_to_bf16(v[x]));
+      }
       if (xrow) {
         const uint2 xv = *reinterpret_cast<const uint2*>(xrow + d0);
         v[0] += bf16_to_f32((uint16_t)xv.x);
@@ -452,18 +463,20 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-template <int D, bool DENSE, bool SPARSE = false>
+template <int D, bool DENSE, bool SPARSE = false, bool FUSED = false>
 static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st) {
   if (dtype == 1)
-    attn_bf16_kernel<D, DENSE, SPARSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
-  else
+    attn_bf16_kernel<D, DENSE, SPARSE, FUSED><<<(unsigned)nblocks, 256, 0, st>>>(a);
+  else if (!FUSED)
     attn_f32_kernel<D, DENSE, SPARSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
+  else
+    return hipErrorInvalidValue;         // the fused layer is bf16 only
   return hipGetLastError();
 }
 
 hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, const void* K, const void* Vt,
                                    int nseq, const AttnSeqDesc* seqs, int Hq, int Hkv, const void* X, void* O,
-                                   hipStream_t st) {
+                                   hipStream_t st, bool fused) {
   const int bm = dtype == 1 ? 128 : 64;        // query rows per block
   AttnArgs a{};
   a.Q = Q; a.K = K; a.Vt = Vt; a.X = X; a.O = O;
@@ -474,14 +487,19 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
     for (int i = 0; i < a.nseg; ++i) {
       const AttnSeqDesc& q = seqs[first + i];
       AttnSeg& g = a.seg[i];
-      g.tok_off = q.tok_off; g.cap_off = q.cap_off; g.L = q.L; g.C = q.C; g.Lp = q.Lp_dev;
+      g.tok_off = q.tok_off; g.cap_off = q.cap_off; g.L = q.L; g.C = q.C; g.Lp = q.Lp_dev; g.idx = q.idx;
       g.blk0 = nblocks;
       g.nmb = (int)((q.L + bm - 1) / bm);
       nblocks += g.nmb * Hq;
     }
     hipError_t e;
-    if (d == 128) e = dense ? run_attn<128, true>(dtype, a, nblocks, st) : run_attn<128, false>(dtype, a, nblocks, st);
-    else e = dense ? run_attn<64, true>(dtype, a, nblocks, st) : run_attn<64, false>(dtype, a, nblocks, st);
+    if (fused)
+      e = d == 128 ? run_attn<128, false, false, true>(dtype, a, nblocks, st)
+                   : run_attn<64, false, false, true>(dtype, a, nblocks, st);
+    else if (d == 128)
+      e = dense ? run_attn<128, true>(dtype, a, nblocks, st) : run_attn<128, false>(dtype, a, nblocks, st);
+    else
+      e = dense ? run_attn<64, true>(dtype, a, nblocks, st) : run_attn<64, false>(dtype, a, nblocks, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -496,7 +514,7 @@ hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const
   a.Hq = Hq; a.Hkv = Hkv; a.scale = (float)(1.0 / sqrt((double)d));
   a.blist = list; a.bcnt = count; a.nbmax = (int)(C / kBlock);
   a.nseg = 1;
-  a.seg[0] = AttnSeg{0, 0, L, C, Lp_dev, 0, (int)((L + bm - 1) / bm)};
+  a.seg[0] = AttnSeg{0, 0, L, C, Lp_dev, nullptr, 0, (int)((L + bm - 1) / bm)};
   const int nblocks = a.seg[0].nmb * Hq;
   return d == 128 ? run_attn<128, false, true>(dtype, a, nblocks, st) : run_attn<64, false, true>(dtype, a, nblocks, st);
 }
@@ -504,8 +522,8 @@ hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const
 hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const void* K,
                             const void* Vt, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
                             int64_t C, const void* X, void* O, hipStream_t st) {
-  const AttnSeqDesc one{0, 0, L, C, Lp_dev};
-  return launch_attention_varlen(dtype, d, dense, Q, K, Vt, 1, &one, Hq, Hkv, X, O, st);
+  const AttnSeqDesc one{0, 0, L, C, Lp_dev, nullptr};
+  return launch_attention_varlen(dtype, d, dense, Q, K, Vt, 1, &one, Hq, Hkv, X, O, st, false);
 }
 
 }  // namespace tsa

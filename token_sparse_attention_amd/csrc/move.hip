@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
     if (r < n) {
       const int64_t t = idx[(size_t)h * L + i0 + r];
       const size_t dst = ((size_t)h * C + i0 + r) * VPR + c;
-      Qh4[dst] = Q4[((size_t)t * Hq + h) * VPR + c];
+      if (Qh4) Qh4[dst] = Q4[((size_t)t * Hq + h) * VPR + c];   // the fused layer reads Q in place
       Kh4[dst] = K4[((size_t)t * Hkv + g) * VPR + c];
       v = V4[((size_t)t * Hkv + g) * VPR + c];
     }
@@ -132,6 +132,41 @@ __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ 
       Y4[e] = X4 ? add_vec<T>(X4[e], o) : o;
     }
   }
+}
+
+// The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fill_unselected_kernel(const int32_t* __restrict__ inv, const T* __restrict__ X,
+                                                              T* __restrict__ Y, int64_t L, int Hq) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  const uint4* X4 = reinterpret_cast<const uint4*>(X);
+  uint4* Y4 = reinterpret_cast<uint4*>(Y);
+  const size_t n = (size_t)L * Hq * VPR;
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
+    const size_t th = e / VPR;
+    const int h = (int)(th % Hq);
+    const int64_t t = (int64_t)(th / Hq);
+    if (inv[(size_t)h * L + t] < 0) Y4[e] = X4 ? X4[e] : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <typename T, int D>
+static hipError_t run_fill_unselected(const int32_t* inv, const void* X, void* Y, int64_t L, int Hq, hipStream_t st) {
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  const size_t n = (size_t)L * Hq * VPR;
+  const unsigned blocks = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  fill_unselected_kernel<T, D><<<blocks, 256, 0, st>>>(inv, static_cast<const T*>(X), static_cast<T*>(Y), L, Hq);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_unselected(int dtype, int d, const int32_t* inv, const void* X, void* Y, int64_t L, int Hq,
+                                  hipStream_t st) {
+  if (X == Y) return hipSuccess;             // in place: those rows already hold X
+  if (dtype == 1)
+    return d == 128 ? run_fill_unselected<uint16_t, 128>(inv, X, Y, L, Hq, st)
+                    : run_fill_unselected<uint16_t, 64>(inv, X, Y, L, Hq, st);
+  return d == 128 ? run_fill_unselected<float, 128>(inv, X, Y, L, Hq, st)
+                  : run_fill_unselected<float, 64>(inv, X, Y, L, Hq, st);
 }
 
 // Index-driven variant (no inverse map): Y must already hold X (or zeros for a pure decompress).

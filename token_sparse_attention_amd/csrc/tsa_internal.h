@@ -50,6 +50,10 @@ hipError_t launch_gather(int dtype, int d, const void* Q, const void* K, const v
                          int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st);
 hipError_t launch_transpose_v(int dtype, int d, const void* V, int64_t L, int Hkv, int64_t C,
                               void* Vt, hipStream_t st);
+// Rows outside every selection: Y[t][h] = X[t][h] (or +0.0 without X) where inv[h][t] < 0; nothing
+// when Y aliases X.  (The fused layer writes the selected rows from the attention epilogue.)
+hipError_t launch_fill_unselected(int dtype, int d, const int32_t* inv, const void* X, void* Y, int64_t L, int Hq,
+                                  hipStream_t st);
 hipError_t launch_scatter(int dtype, int d, const void* Oh, const int32_t* idx, const int32_t* inv,
                           const int32_t* Lp_dev, const void* X, void* Y, int64_t L, int Hq,
                           int64_t C, hipStream_t st);
@@ -77,13 +81,17 @@ hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const v
 // [Hq][d][C] start at element Hq*d*cap_off, L' is read from Lp_dev, and L bounds the grid (L' <= L).
 // Dense: tokens [tok_off, tok_off + L) of Q/K/X/Y; its Vt region [Hkv][d][C] starts at element
 // Hkv*d*cap_off.  Longer sequences listed first are scheduled first.
+// Fused (compressed, bf16): Q is the uncompressed [tokens][Hq][d] input, query row i of head h is
+// token tok_off + idx[h][i] (idx [Hq][L] per sequence), and the output row is written to O (= Y)
+// at that token, plus X when given, rounded as tsa_scatter_residual rounds; Kh/Vht as compressed.
 struct AttnSeqDesc {
   int64_t tok_off, cap_off, L, C;
   const int32_t* Lp_dev;
+  const int32_t* idx;
 };
 hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, const void* K, const void* Vt,
                                    int nseq, const AttnSeqDesc* seqs, int Hq, int Hkv, const void* X, void* O,
-                                   hipStream_t st);
+                                   hipStream_t st, bool fused = false);
 // Compressed attention restricted to the listed key blocks of every query block (launch_block_select's
 // list and count, NB = C / kBlock).
 hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const void* Kh, const void* Vht,
