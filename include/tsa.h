@@ -109,7 +109,8 @@ int tsa_select(const tsa_shape* s, const float* s_h, const int32_t* Lp_dev, int3
 
 /* Stage 4a -- compress (notes, "Key design 1"; article 1.1 gather):
  *   Qh[h][i] = Q[idx[h][i]][h],  Kh[h][i] = K[idx[h][i]][g],  Vht[h][.][i] = V[idx[h][i]][g]
- * for i < L'; rows / columns L' .. C-1 are written with zeros.  Bit-exact copies. */
+ * for i < L'.  Bit-exact copies.  Rows (Vht: columns) at and past L' hold unspecified values; no
+ * entry point reads them. */
 int tsa_gather(const tsa_shape* s, const void* Q, const void* K, const void* V, const int32_t* idx,
                const int32_t* Lp_dev, void* Qh, void* Kh, void* Vht, void* stream);
 

@@ -2,8 +2,8 @@
 // section 1.1 gather / zeros_like + scatter_): pure data movement in 16-byte vectors.
 //
 // gather : per query head, rows idx[h][0..L') of Q, K, V -> dense Qh, Kh [Hq][C][d] and the
-//          transposed Vht [Hq][d][C] (a 64-row tile is staged in LDS and written column-major so
-//          the stores stay contiguous).
+//          transposed Vht [Hq][d][C] (bf16: 8 x 8 blocks transposed in registers; fp32: a 64-row
+//          tile staged in LDS and written column-major so the stores stay contiguous).
 // scatter: Y[t][h] = X[t][h] + Oh[h][inv[h][t]] for selected t, X[t][h] otherwise (float32 sum,
 //          one rounding); without X the selected rows are copied and the others are +0.0.
 #include "kern_common.h"
@@ -55,6 +55,82 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
     uint4 w;
     __builtin_memcpy(&w, vals, 16);
     *reinterpret_cast<uint4*>(Vht + ((size_t)h * D + dd) * C + i0 + j0) = w;
+  }
+}
+
+// bf16: a thread owns one 16-byte chunk (8 columns) of 8 consecutive compressed rows.  It loads that
+// chunk of the 8 gathered rows (16 threads cover a 256-byte row, so the loads stay coalesced) and
+// transposes the 8 x 8 block of 16-bit values in registers with byte permutes.  The resulting
+// 16-byte pieces (8 rows of one column) are regrouped through LDS, [column][row] with a XOR swizzle
+// of the piece slot, so that each column's run of TR rows leaves as contiguous 16-byte stores.
+template <int D>
+__global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
+                                                          int64_t C, uint16_t* __restrict__ Qh, uint16_t* __restrict__ Kh,
+                                                          uint16_t* __restrict__ Vht) {
+  constexpr int VPR = D / 8;            // 16-byte chunks per row
+  constexpr int NG = 256 / VPR;         // groups of 8 rows per block
+  constexpr int TR = NG * 8;            // rows per block (128 for d = 128, 256 for d = 64)
+  constexpr int PPC = TR / 8;           // 16-byte pieces per column in the block (= NG)
+  __shared__ uint4 tile[D * PPC];       // [column][piece], piece slot swizzled
+  // block -> (KV group, row tile, head of the group): the G heads of one (group, tile) pair are
+  // consecutive blocks of one XCD (blockIdx % 8), so its L2 serves the K/V rows they share
+  const int G = Hq / Hkv;
+  const int64_t ntiles = (L + TR - 1) / TR;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int64_t pair = (int64_t)(slot / G) * 8 + xcd;
+  if (pair >= ntiles * Hkv) return;
+  const int g = (int)(pair % Hkv), h = g * G + slot % G;
+  const int64_t Lp = Lp_dev[0];
+  const int64_t b0 = (pair / Hkv) * TR;
+  if (b0 >= Lp) return;
+  const int c = threadIdx.x % VPR, grp = threadIdx.x / VPR;
+  const int64_t r0 = b0 + grp * 8;
+  const uint4* Q4 = reinterpret_cast<const uint4*>(Q);
+  const uint4* K4 = reinterpret_cast<const uint4*>(K);
+  const uint4* V4 = reinterpret_cast<const uint4*>(V);
+  uint4* Qh4 = reinterpret_cast<uint4*>(Qh);
+  uint4* Kh4 = reinterpret_cast<uint4*>(Kh);
+  uint32_t v[8][4];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = r0 + u;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (i < Lp) {
+      const int64_t t = idx[(size_t)h * L + i];
+      const size_t dst = ((size_t)h * C + i) * VPR + c;
+      if (Qh4) Qh4[dst] = Q4[((size_t)t * Hq + h) * VPR + c];   // the fused layer reads Q in place
+      Kh4[dst] = K4[((size_t)t * Hkv + g) * VPR + c];
+      x = V4[((size_t)t * Hkv + g) * VPR + c];
+    }
+    v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+  }
+  // column 2j of the chunk is the low half of word j of every row, column 2j+1 the high half; word
+  // m of a column piece pairs rows 2m (low) and 2m+1 (high).  Piece grp of column col sits in slot
+  // grp ^ (col % PPC) of that column's LDS row.
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint4 lo, hi;
+    lo.x = __builtin_amdgcn_perm(v[1][j], v[0][j], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(v[3][j], v[2][j], 0x05040100u);
+    lo.z = __builtin_amdgcn_perm(v[5][j], v[4][j], 0x05040100u);
+    lo.w = __builtin_amdgcn_perm(v[7][j], v[6][j], 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(v[1][j], v[0][j], 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(v[3][j], v[2][j], 0x07060302u);
+    hi.z = __builtin_amdgcn_perm(v[5][j], v[4][j], 0x07060302u);
+    hi.w = __builtin_amdgcn_perm(v[7][j], v[6][j], 0x07060302u);
+    const int col = 8 * c + 2 * j;
+    tile[col * PPC + (grp ^ (col % PPC))] = lo;
+    tile[(col + 1) * PPC + (grp ^ ((col + 1) % PPC))] = hi;
+  }
+  __syncthreads();
+  // each column's TR rows: PPC consecutive lanes store its PPC pieces contiguously
+  const int64_t nrows = Lp - b0 < TR ? Lp - b0 : TR;
+  for (int e = threadIdx.x; e < D * PPC; e += 256) {
+    const int col = e / PPC, q = e % PPC;
+    if ((int64_t)q * 8 >= nrows) continue;
+    *reinterpret_cast<uint4*>(Vht + ((size_t)h * D + col) * C + b0 + 8 * q) = tile[col * PPC + (q ^ (col % PPC))];
   }
 }
 
@@ -135,25 +211,25 @@ __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ 
 }
 
 // The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
+// One (token, head) pair per thread: the inverse map is read once and only unselected rows move.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fill_unselected_kernel(const int32_t* __restrict__ inv, const T* __restrict__ X,
                                                               T* __restrict__ Y, int64_t L, int Hq) {
   constexpr int VPR = D * (int)sizeof(T) / 16;
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
   uint4* Y4 = reinterpret_cast<uint4*>(Y);
-  const size_t n = (size_t)L * Hq * VPR;
+  const size_t n = (size_t)L * Hq;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    const size_t th = e / VPR;
-    const int h = (int)(th % Hq);
-    const int64_t t = (int64_t)(th / Hq);
-    if (inv[(size_t)h * L + t] < 0) Y4[e] = X4 ? X4[e] : make_uint4(0, 0, 0, 0);
+    if (inv[e] >= 0) continue;              // inv is [Hq][L]: consecutive threads, consecutive tokens
+    const size_t row = (size_t)(e % L) * Hq + e / L;
+#pragma unroll 4
+    for (int c = 0; c < VPR; ++c) Y4[row * VPR + c] = X4 ? X4[row * VPR + c] : make_uint4(0, 0, 0, 0);
   }
 }
 
 template <typename T, int D>
 static hipError_t run_fill_unselected(const int32_t* inv, const void* X, void* Y, int64_t L, int Hq, hipStream_t st) {
-  constexpr int VPR = D * (int)sizeof(T) / 16;
-  const size_t n = (size_t)L * Hq * VPR;
+  const size_t n = (size_t)L * Hq;
   const unsigned blocks = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
   fill_unselected_kernel<T, D><<<blocks, 256, 0, st>>>(inv, static_cast<const T*>(X), static_cast<T*>(Y), L, Hq);
   return hipGetLastError();
@@ -205,10 +281,20 @@ template <typename T, int D>
 static hipError_t run_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                              const int32_t* Lp_dev, int64_t L, int Hq, int Hkv, int64_t C, void* Qh,
                              void* Kh, void* Vht, hipStream_t st) {
-  const dim3 grid((unsigned)((L + kTileRows - 1) / kTileRows), (unsigned)Hq);
-  gather_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(Q), static_cast<const T*>(K),
-                                            static_cast<const T*>(V), idx, Lp_dev, L, Hq, Hkv, C,
-                                            static_cast<T*>(Qh), static_cast<T*>(Kh), static_cast<T*>(Vht));
+  if constexpr (sizeof(T) == 2) {
+    constexpr int TR = 256 / (D / 8) * 8;
+    const int64_t pairs = (L + TR - 1) / TR * Hkv;
+    const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
+    gather_bf16_kernel<D><<<nblk, 256, 0, st>>>(static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
+                                                static_cast<const uint16_t*>(V), idx, Lp_dev, L, Hq, Hkv, C,
+                                                static_cast<uint16_t*>(Qh), static_cast<uint16_t*>(Kh),
+                                                static_cast<uint16_t*>(Vht));
+  } else {
+    const dim3 grid((unsigned)((L + kTileRows - 1) / kTileRows), (unsigned)Hq);
+    gather_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(Q), static_cast<const T*>(K),
+                                              static_cast<const T*>(V), idx, Lp_dev, L, Hq, Hkv, C,
+                                              static_cast<T*>(Qh), static_cast<T*>(Kh), static_cast<T*>(Vht));
+  }
   return hipGetLastError();
 }
 
