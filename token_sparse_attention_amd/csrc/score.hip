@@ -211,13 +211,18 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restr
                                                          double c, double2* __restrict__ part,
                                                          const double2* __restrict__ rowstat, float* __restrict__ s_h) {
   constexpr int KST = D / 32;                  // K-steps of 32 over the head dim
-  __shared__ __attribute__((aligned(16))) uint16_t qs[kMRows * D];
-  __shared__ float wm[4][kMRows];              // pass 1: per-wave partial max ...
-  __shared__ double wz[4][kMRows];             // ... and sum
-  __shared__ float bm[kMRows];                 // pass 1: block running max / sum; pass 2: row max
-  __shared__ double bz[kMRows];                //                                 pass 2: 1 / Z
+  // LDS sized by the launch for Rp rows (score_mfma_smem): the recent queries, then per-wave partial
+  // max / sum (pass 1) and the block's running max / sum, or the rows' max and 1 / Z (pass 2)
+  extern __shared__ __attribute__((aligned(16))) char score_smem[];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
   const int G = Hq / Hkv, Rp = G * qp, MT = Rp / 16;
+  uint16_t* qs = reinterpret_cast<uint16_t*>(score_smem);
+  double* wz_ = reinterpret_cast<double*>(score_smem + (size_t)Rp * D * 2);
+  double* bz = wz_ + 4 * Rp;
+  float* wm_ = reinterpret_cast<float*>(bz + Rp);
+  float* bm = wm_ + 4 * Rp;
+  auto wm = [&](int v, int r) -> float& { return wm_[v * Rp + r]; };
+  auto wz = [&](int v, int r) -> double& { return wz_[v * Rp + r]; };
   const int64_t nblk = gridDim.x;
   for (int e = tid; e < Rp * (D / 8); e += 256) {
     const int row = e / (D / 8), c8 = e % (D / 8), j = row / qp, i = row % qp;
@@ -285,8 +290,8 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restr
           }
           zs = shfl_sum16(zs);
           if (l16 == 0) {
-            wm[w][row] = zm;
-            wz[w][row] = zs;
+            wm(w, row) = zm;
+            wz(w, row) = zs;
           }
         }
       } else {
@@ -324,13 +329,13 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restr
       for (int r = tid; r < Rp; r += 256) {
         float m = bm[r];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) m = fmaxf(m, wm[v][r]);
+        for (int v = 0; v < 4; ++v) m = fmaxf(m, wm(v, r));
         double Z = 0.0;
         if (m > -INFINITY) {
           if (bz[r] > 0.0) Z += bz[r] * exp2(((double)bm[r] - (double)m) * c);
 #pragma unroll
           for (int v = 0; v < 4; ++v)
-            if (wz[v][r] > 0.0) Z += wz[v][r] * exp2(((double)wm[v][r] - (double)m) * c);
+            if (wz(v, r) > 0.0) Z += wz(v, r) * exp2(((double)wm(v, r) - (double)m) * c);
         }
         bm[r] = m;
         bz[r] = Z;
@@ -343,6 +348,9 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restr
 }
 
 int score_rows_padded(int Hq, int Hkv, int q) { return (Hq / Hkv) * ((q + 15) / 16 * 16); }
+
+// dynamic LDS of score_mfma_kernel for Rp rows of head dimension D
+static size_t score_mfma_smem(int Rp, int D) { return (size_t)Rp * D * 2 + (size_t)Rp * 5 * 8 + (size_t)Rp * 5 * 4; }
 
 static bool use_mfma(int dtype, int Hq, int Hkv, int q) {
   return dtype == 1 && score_rows_padded(Hq, Hkv, q) <= kMRows;
@@ -359,10 +367,19 @@ static hipError_t run_score_mfma(const void* Q, const void* K, int64_t L, int Hq
   const dim3 grid((unsigned)((L + nsub * kMSub - 1) / (nsub * kMSub)), (unsigned)Hkv);
   const uint16_t* Qt = static_cast<const uint16_t*>(Q);
   const uint16_t* Kt = static_cast<const uint16_t*>(K);
-  score_mfma_kernel<D, 1><<<grid, 256, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
+  const size_t smem = score_mfma_smem(Rp, D);
+  if (smem > 48 * 1024) {                     // up to 79 KB for 256 rows: raise the dynamic-LDS limit
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel<D, 1>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel<D, 2>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+  }
+  score_mfma_kernel<D, 1><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
   const int64_t nrows = (int64_t)Hkv * Rp;
   score_combine_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(part, nrows, grid.x, scale, rowstat);
-  score_mfma_kernel<D, 2><<<grid, 256, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
+  score_mfma_kernel<D, 2><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
   return hipGetLastError();
 }
 
