@@ -31,8 +31,8 @@ StageWs stage_layout(const tsa_shape* s) {
   StageWs w;
   size_t o = 0;
   auto take = [&](size_t n) { size_t at = o; o += up(n); return at; };
-  w.partials = take(score_partial_bytes(s->L, s->Hq, s->q));
-  w.rowstat = take(score_rowstat_bytes(s->Hq, s->q));
+  w.partials = take(score_partial_bytes(s->L, s->Hq, s->Hkv, s->q));
+  w.rowstat = take(score_rowstat_bytes(s->Hq, s->Hkv, s->q));
   w.S = take((size_t)s->L * sizeof(double));
   w.tilesum = take((size_t)layer_tiles(s->L) * sizeof(double));
   w.bhist = take((size_t)kRadixPasses * 2 * kRadixBins * sizeof(uint64_t));

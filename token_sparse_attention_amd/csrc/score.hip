@@ -19,15 +19,21 @@ constexpr int kQChunk = 32;       // recent-query rows staged in LDS at a time
 
 int64_t score_blocks(int64_t L) { return (L + kScoreKeys - 1) / kScoreKeys; }
 
-size_t score_partial_bytes(int64_t L, int Hq, int q) {
+size_t score_partial_bytes(int64_t L, int Hq, int Hkv, int q) {
   // float64 path: a partial per row, 256-key block and wave; matrix-core path: a partial per padded
-  // row and block of at least 256 keys (at most 16 * Hq * ceil(q/16) rows)
+  // row (each group's rows padded to a multiple of 32, heads to 16 or a multiple of 32) and block of
+  // at least 256 keys
   const size_t vec = (size_t)Hq * q * score_blocks(L) * (kScoreKeys / kWave);
-  const size_t mfma = (size_t)Hq * ((q + 15) / 16 * 16) * ((L + 255) / 256);
+  const size_t rows = (size_t)Hkv * (((Hq / Hkv) * (q <= 16 ? 16 : (q + 31) / 32 * 32) + 31) / 32 * 32);
+  const size_t mfma = rows * ((L + 255) / 256);
   return (vec > mfma ? vec : mfma) * sizeof(double2);
 }
 
-size_t score_rowstat_bytes(int Hq, int q) { return (size_t)Hq * ((q + 15) / 16 * 16) * sizeof(double2); }
+size_t score_rowstat_bytes(int Hq, int Hkv, int q) {
+  const size_t vec = (size_t)Hq * q;
+  const size_t rows = (size_t)Hkv * (((Hq / Hkv) * (q <= 16 ? 16 : (q + 31) / 32 * 32) + 31) / 32 * 32);
+  return (vec > rows ? vec : rows) * sizeof(double2);
+}
 
 template <typename T, int D>
 __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&r)[D]) {
@@ -171,195 +177,247 @@ static hipError_t run_score(const void* Q, const void* K, int64_t L, int Hq, int
 }
 
 // ---- bf16 path on the matrix cores ---------------------------------------------------------------
-// Logits z = <Q[p][h], K[t][g]> come from v_mfma_f32_16x16x32_bf16 (bf16 products are exact in
-// float32; only the accumulation rounds).  A = 16 recent-query rows of one head (each head's q rows
-// padded to a multiple of 16 and staged in LDS), B = 16 keys; a wave owns 64 keys of a 256-key
-// sub-chunk and a block walks four sub-chunks (1024 keys) of one KV group.
-//   pass 1: per row, max and sum of exponentials over the wave's keys (cross-lane in the 16 lanes of
-//           a row group), merged over waves and sub-chunks in LDS: one (max, sum) partial per
-//           row and block;
-//   pass 2: w = exp(z - m) / Z, summed over each M-tile's 16 rows and over the head's M-tiles.
-// Every exponential is exp2 of (z - m) * log2(e) / sqrt(d) formed in float64 from the float32
-// logits, evaluated as exp2f(hi) * (1 + lo * ln 2) with hi + lo that argument, and all sums are
-// float64: about 1e-7 relative, far inside the selection's 1e-6 tie band.
+// Logits z = <Q[p][h], K[t][g]> come from v_mfma_f32_32x32x16_bf16 (bf16 products are exact in
+// float32; only the accumulation rounds).  The recent-query rows of a KV group are staged in LDS,
+// each head's q rows padded to 16 (q <= 16) or to a multiple of 32, the group to a multiple of 32.
+// A wave owns 64 keys (two blocks of 32) of each 256-key sub-chunk; a workgroup walks nsub
+// sub-chunks of one KV group.  The product is oriented so that every reduction is lane-local:
+//   pass 1: D = K Q^T, a lane holds 16 keys of ONE row: it keeps that row's running (max, sum of
+//           exponentials) in registers over all of the workgroup's keys; the two lanes sharing a
+//           row and the four waves are merged once at the end, one (max, sum) partial per row and
+//           workgroup;
+//   pass 2: D = Q K^T, a lane holds 16 rows of ONE key: the weights exp(z - m) / Z are summed over
+//           the head's rows in the lane, plus one exchange with the lane holding the other rows.
+// Causal masks are applied only in workgroups that reach the recent window.  Every exponential is
+// exp2 of z * log2(e) / sqrt(d) - m * log2(e) / sqrt(d), formed with one float64 fma from the float32
+// logit, evaluated as exp2f(hi) * (1 + lo * ln 2) with hi + lo that argument; all sums are float64:
+// about 1e-7 relative, far inside the selection's 1e-6 tie band.
 constexpr int kMSub = 256, kMRows = 256;   // keys per sub-chunk (a block walks nsub of them); max rows
 
 typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
-typedef float f32x4s_t __attribute__((ext_vector_type(4)));
+typedef float f32x16s_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ double exp2_rel(float z, float m, double c) {
-  const double y = ((double)z - (double)m) * c;
+// exp2(z * c - mc) with the argument formed in float64
+__device__ __forceinline__ double exp2_mc(float z, double c, double mc) {
+  const double y = fma((double)z, c, -mc);
   const float hi = (float)y;
   const float lo = (float)(y - (double)hi);
   return (double)(__builtin_amdgcn_exp2f(hi) * fmaf(lo, 0.69314718055994531f, 1.0f));
 }
 
-__device__ __forceinline__ double shfl_sum16(double v) {     // over the 16 lanes of a row group
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-__device__ __forceinline__ float shfl_max16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
+// LDS slot of 16-byte chunk c8 of staged query row r (XOR swizzle: 16 consecutive rows' reads of
+// one chunk land on distinct banks)
+template <int D>
+__device__ __forceinline__ int qslot(int r, int c8) { return r * D + 8 * (c8 ^ (r & (D / 8 - 1))); }
 
-template <int D, int PASS>
-__global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                         int64_t L, int Hq, int Hkv, int q, int qp, int nsub,
-                                                         double c, double2* __restrict__ part,
-                                                         const double2* __restrict__ rowstat, float* __restrict__ s_h) {
-  constexpr int KST = D / 32;                  // K-steps of 32 over the head dim
-  // LDS sized by the launch for Rp rows (score_mfma_smem): the recent queries, then per-wave partial
-  // max / sum (pass 1) and the block's running max / sum, or the rows' max and 1 / Z (pass 2)
-  extern __shared__ __attribute__((aligned(16))) char score_smem[];
-  const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, lg = lane >> 4;
-  const int G = Hq / Hkv, Rp = G * qp, MT = Rp / 16;
-  uint16_t* qs = reinterpret_cast<uint16_t*>(score_smem);
-  double* wz_ = reinterpret_cast<double*>(score_smem + (size_t)Rp * D * 2);
-  double* bz = wz_ + 4 * Rp;
-  float* wm_ = reinterpret_cast<float*>(bz + Rp);
-  float* bm = wm_ + 4 * Rp;
-  auto wm = [&](int v, int r) -> float& { return wm_[v * Rp + r]; };
-  auto wz = [&](int v, int r) -> double& { return wz_[v * Rp + r]; };
-  const int64_t nblk = gridDim.x;
-  for (int e = tid; e < Rp * (D / 8); e += 256) {
+// Stages the group's recent-query rows (row = j * qp + i for head j, recent query i; zero padding)
+template <int D>
+__device__ __forceinline__ void stage_queries(const uint16_t* __restrict__ Q, uint16_t* qs, int64_t L, int Hq, int g,
+                                              int G, int q, int qp, int Rp) {
+  for (int e = threadIdx.x; e < Rp * (D / 8); e += 256) {
     const int row = e / (D / 8), c8 = e % (D / 8), j = row / qp, i = row % qp;
     uint4 v = make_uint4(0, 0, 0, 0);
-    if (i < q) v = *reinterpret_cast<const uint4*>(Q + ((size_t)(L - q + i) * Hq + g * G + j) * D + 8 * c8);
-    *reinterpret_cast<uint4*>(&qs[row * D + 8 * c8]) = v;
+    if (j < G && i < q) v = *reinterpret_cast<const uint4*>(Q + ((size_t)(L - q + i) * Hq + g * G + j) * D + 8 * c8);
+    *reinterpret_cast<uint4*>(&qs[qslot<D>(row, c8)]) = v;
   }
-  for (int r = tid; r < Rp; r += 256) {
-    if (PASS == 1) {
-      bm[r] = -INFINITY;
-      bz[r] = 0.0;
-    } else {
-      const double2 ms = rowstat[(size_t)g * Rp + r];
-      bm[r] = (float)ms.x;
-      bz[r] = ms.y;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void score_p1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                       int64_t L, int Hq, int Hkv, int q, int qp, int nsub, double c,
+                                                       double2* __restrict__ part) {
+  constexpr int KST = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char score_smem[];
+  const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int G = Hq / Hkv, Rp = (G * qp + 31) / 32 * 32, MB = Rp / 32;
+  uint16_t* qs = reinterpret_cast<uint16_t*>(score_smem);
+  double* wz = reinterpret_cast<double*>(score_smem + (size_t)Rp * D * 2);   // [4][Rp]
+  float* wm = reinterpret_cast<float*>(wz + 4 * Rp);                         // [4][Rp]
+  stage_queries<D>(Q, qs, L, Hq, g, G, q, qp, Rp);
+  __syncthreads();
+
+  const int64_t bkeys = (int64_t)nsub * kMSub;
+  // every key of the workgroup precedes every recent query: no causal mask
+  const bool open = (int64_t)(blockIdx.x + 1) * bkeys <= L - q + 1;
+  float M[kMRows / 32];
+  double S[kMRows / 32];
+#pragma unroll
+  for (int mb = 0; mb < kMRows / 32; ++mb) {
+    M[mb] = -INFINITY;
+    S[mb] = 0.0;
+  }
+  for (int sub = 0; sub < nsub; ++sub) {
+#pragma unroll 1
+    for (int kb = 0; kb < 2; ++kb) {
+      // one block of 32 keys at a time (keeps registers low); z[r] below is key kbase + 8 (r / 4) +
+      // 4 hf + r % 4 of the lane's row
+      const int64_t kbase = (int64_t)blockIdx.x * bkeys + sub * kMSub + 64 * w + 32 * kb;
+      bf16x8s_t kf[KST];
+      {
+        const int64_t key = kbase + l32;
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks)
+          kf[ks] = key < L ? *reinterpret_cast<const bf16x8s_t*>(K + ((size_t)key * Hkv + g) * D + 16 * ks + 8 * hf)
+                           : bf16x8s_t{};
+      }
+#pragma unroll
+      for (int mb = 0; mb < kMRows / 32; ++mb) {
+        if (mb >= MB) break;
+        const int row = 32 * mb + l32, j = row / qp, i = row % qp;
+        // keys kbase + rel with rel <= lim are visible to this lane's row (none for padding rows)
+        int lim = -1;
+        if (j < G && i < q) {
+          const int64_t last = open ? kbase + 63 : L - q + i;     // the row's last visible key
+          lim = (int)(last - kbase < 63 ? (last - kbase < -1 ? -1 : last - kbase) : 63);
+        }
+        bf16x8s_t qf[KST];
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks) qf[ks] = *reinterpret_cast<const bf16x8s_t*>(&qs[qslot<D>(row, 2 * ks + hf)]);
+        f32x16s_t z = {};
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], z, 0, 0, 0);
+        // masked logits become -1e30: their exponential below is exactly 0 (with a finite argument)
+        float zm = -1e30f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          z[r] = 8 * (r >> 2) + 4 * hf + (r & 3) <= lim ? z[r] : -1e30f;
+          zm = fmaxf(zm, z[r]);
+        }
+        if (zm > -1e29f) {                   // some key visible
+          const float mn = fmaxf(M[mb], zm);
+          const double mc = (double)mn * c;
+          double acc = 0.0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc += exp2_mc(z[r], c, mc);
+          const double f = M[mb] > -INFINITY ? exp2_mc(M[mb], c, mc) : 0.0;
+          S[mb] = S[mb] * f + acc;
+          M[mb] = mn;
+        }
+      }
+    }
+  }
+  // the two lanes of a row, then the four waves
+#pragma unroll
+  for (int mb = 0; mb < kMRows / 32; ++mb) {
+    if (mb >= MB) break;
+    const float m2 = __shfl_xor(M[mb], 32, kWave);
+    const double s2 = __shfl_xor(S[mb], 32, kWave);
+    const float mn = fmaxf(M[mb], m2);
+    double Z = 0.0;
+    if (mn > -INFINITY) {
+      const double mc = (double)mn * c;
+      if (M[mb] > -INFINITY) Z += S[mb] * exp2_mc(M[mb], c, mc);
+      if (m2 > -INFINITY) Z += s2 * exp2_mc(m2, c, mc);
+    }
+    if (hf == 0) {
+      wm[w * Rp + 32 * mb + l32] = mn;
+      wz[w * Rp + 32 * mb + l32] = Z;
     }
   }
   __syncthreads();
-
-  // Blocks whose keys all precede the recent window, with every padded row real (q % 16 == 0), see
-  // every key from every row: no masks.
-  const int64_t bkeys = (int64_t)nsub * kMSub;
-  const bool open = (int64_t)(blockIdx.x + 1) * bkeys <= L - q + 1 && q == qp;
-  for (int sub = 0; sub < nsub; ++sub) {
-    const int64_t key0 = ((int64_t)blockIdx.x * bkeys + sub * kMSub) + 64 * w;
-    bf16x8s_t kf[4][KST];
+  const int64_t nblk = gridDim.x;
+  for (int r = tid; r < Rp; r += 256) {
+    float m = -INFINITY;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const int64_t key = key0 + 16 * n + l16;
+    for (int v = 0; v < 4; ++v) m = fmaxf(m, wm[v * Rp + r]);
+    double Z = 0.0;
+    if (m > -INFINITY) {
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks)
-        kf[n][ks] = key < L ? *reinterpret_cast<const bf16x8s_t*>(K + ((size_t)key * Hkv + g) * D + 32 * ks + 8 * lg)
-                            : bf16x8s_t{};
+      for (int v = 0; v < 4; ++v)
+        if (wz[v * Rp + r] > 0.0) Z += wz[v * Rp + r] * exp2(((double)wm[v * Rp + r] - (double)m) * c);
     }
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int mt = 0; mt < MT; ++mt) {
-      f32x4s_t z[4] = {f32x4s_t{}, f32x4s_t{}, f32x4s_t{}, f32x4s_t{}};
-#pragma unroll
-      for (int ks = 0; ks < KST; ++ks) {
-        const bf16x8s_t a = *reinterpret_cast<const bf16x8s_t*>(&qs[(16 * mt + l16) * D + 32 * ks + 8 * lg]);
-#pragma unroll
-        for (int n = 0; n < 4; ++n) z[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[n][ks], z[n], 0, 0, 0);
-      }
-      // z[n][r]: row 16*mt + 4*lg + r, key key0 + 16*n + l16
-      const int j = (16 * mt) / qp;
-      if (PASS == 1) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * lg + r, i = row % qp;
-          const int64_t p = L - q + i;
-          float zm = -INFINITY;
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int64_t key = key0 + 16 * n + l16;
-            if (open || (i < q && key <= p)) zm = fmaxf(zm, z[n][r]);
-          }
-          zm = shfl_max16(zm);
-          double zs = 0.0;
-          if (zm > -INFINITY) {
-#pragma unroll
-            for (int n = 0; n < 4; ++n) {
-              const int64_t key = key0 + 16 * n + l16;
-              if (open || (i < q && key <= p)) zs += exp2_rel(z[n][r], zm, c);
-            }
-          }
-          zs = shfl_sum16(zs);
-          if (l16 == 0) {
-            wm(w, row) = zm;
-            wz(w, row) = zs;
-          }
-        }
-      } else {
-        double cs[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * mt + 4 * lg + r, i = row % qp;
-          const int64_t p = L - q + i;
-          const float m = bm[row];
-          const double iz = bz[row];
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int64_t key = key0 + 16 * n + l16;
-            if (open || (i < q && key <= p)) cs[n] += exp2_rel(z[n][r], m, c) * iz;
-          }
-        }
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-          cs[n] += __shfl_xor(cs[n], 16, kWave);
-          cs[n] += __shfl_xor(cs[n], 32, kWave);
-          acc[n] += cs[n];
-        }
-        if ((16 * (mt + 1)) % qp == 0) {       // last M-tile of head j: store its column sums
-#pragma unroll
-          for (int n = 0; n < 4; ++n) {
-            const int64_t key = key0 + 16 * n + l16;
-            if (lg == 0 && key < L) s_h[(size_t)(g * G + j) * L + key] = (float)acc[n];
-            acc[n] = 0.0;
-          }
-        }
-      }
-    }
-    if (PASS == 1) {                            // merge the four waves into the block's running state
-      __syncthreads();
-      for (int r = tid; r < Rp; r += 256) {
-        float m = bm[r];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) m = fmaxf(m, wm(v, r));
-        double Z = 0.0;
-        if (m > -INFINITY) {
-          if (bz[r] > 0.0) Z += bz[r] * exp2(((double)bm[r] - (double)m) * c);
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            if (wz(v, r) > 0.0) Z += wz(v, r) * exp2(((double)wm(v, r) - (double)m) * c);
-        }
-        bm[r] = m;
-        bz[r] = Z;
-      }
-      __syncthreads();
-    }
+    part[((size_t)g * Rp + r) * nblk + blockIdx.x] = make_double2(m, Z);
   }
-  if (PASS == 1)
-    for (int r = tid; r < Rp; r += 256) part[((size_t)g * Rp + r) * nblk + blockIdx.x] = make_double2(bm[r], bz[r]);
 }
 
-int score_rows_padded(int Hq, int Hkv, int q) { return (Hq / Hkv) * ((q + 15) / 16 * 16); }
+template <int D>
+__global__ __launch_bounds__(256, 2) void score_p2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                       int64_t L, int Hq, int Hkv, int q, int qp, int nsub, double c,
+                                                       const double2* __restrict__ rowstat, float* __restrict__ s_h) {
+  constexpr int KST = D / 16;
+  extern __shared__ __attribute__((aligned(16))) char score_smem[];
+  const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
+  const int G = Hq / Hkv, Rp = (G * qp + 31) / 32 * 32, MB = Rp / 32;
+  uint16_t* qs = reinterpret_cast<uint16_t*>(score_smem);
+  double2* rc = reinterpret_cast<double2*>(score_smem + (size_t)Rp * D * 2);   // per row: m * c, 1 / Z
+  stage_queries<D>(Q, qs, L, Hq, g, G, q, qp, Rp);
+  for (int r = tid; r < Rp; r += 256) {
+    const double2 ms = rowstat[(size_t)g * Rp + r];
+    const bool ok = r / qp < G && r % qp < q && ms.x > -INFINITY;
+    rc[r] = ok ? make_double2(ms.x * c, ms.y) : make_double2(0.0, 0.0);   // 1 / Z = 0: no such row
+  }
+  __syncthreads();
 
-// dynamic LDS of score_mfma_kernel for Rp rows of head dimension D
-static size_t score_mfma_smem(int Rp, int D) { return (size_t)Rp * D * 2 + (size_t)Rp * 5 * 8 + (size_t)Rp * 5 * 4; }
+  const int64_t bkeys = (int64_t)nsub * kMSub;
+  const bool open = (int64_t)(blockIdx.x + 1) * bkeys <= L - q + 1;
+  for (int sub = 0; sub < nsub; ++sub) {
+#pragma unroll 1
+    for (int kb = 0; kb < 2; ++kb) {
+      // this lane's key and its fragments (one block of 32 keys at a time keeps registers low)
+      const int64_t key = (int64_t)blockIdx.x * bkeys + sub * kMSub + 64 * w + 32 * kb + l32;
+      bf16x8s_t kf[KST];
+#pragma unroll
+      for (int ks = 0; ks < KST; ++ks)
+        kf[ks] = key < L ? *reinterpret_cast<const bf16x8s_t*>(K + ((size_t)key * Hkv + g) * D + 16 * ks + 8 * hf)
+                         : bf16x8s_t{};
+      // visible to recent query i iff key - (L - q) <= i (always in workgroups before the window)
+      const int64_t kr64 = key - (L - q);
+      const int kr = open ? -1 : (int)(kr64 < -1 ? -1 : (kr64 > 1 << 20 ? 1 << 20 : kr64));
+      double csA = 0.0, csB = 0.0;              // the current head's rows (qp = 16: two heads)
+#pragma unroll 1
+      for (int mb = 0; mb < MB; ++mb) {
+        bf16x8s_t qf[KST];
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks)
+          qf[ks] = *reinterpret_cast<const bf16x8s_t*>(&qs[qslot<D>(32 * mb + l32, 2 * ks + hf)]);
+        f32x16s_t z = {};
+#pragma unroll
+        for (int ks = 0; ks < KST; ++ks) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], z, 0, 0, 0);
+        // z[r]: row 32 mb + 8 (r / 4) + 4 hf + r % 4 (its constants are LDS broadcasts: every lane
+        // of a half reads the same row), recent-query index ibase + that offset (qp = 16: mod 16)
+        const int ibase = qp == 16 ? 0 : (32 * mb) % qp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int i = qp == 16 ? off - 16 * (r >> 3) : ibase + off;
+          const double2 rcr = rc[32 * mb + off];
+          const float zv = kr <= i ? z[r] : -1e30f;             // masked: weight exactly 0
+          const double wgt = exp2_mc(zv, c, rcr.x) * rcr.y;
+          if (qp == 16 && r >= 8) csB += wgt;
+          else csA += wgt;
+        }
+        if (qp == 16 || (32 * (mb + 1)) % qp == 0) {     // the block ends a head (qp = 16: two)
+          const int jA = qp == 16 ? 2 * mb : (32 * mb) / qp;
+          const double a = csA + __shfl_xor(csA, 32, kWave);
+          if (hf == 0 && key < L && jA < G) s_h[(size_t)(g * G + jA) * L + key] = (float)a;
+          if (qp == 16) {
+            const double bsum = csB + __shfl_xor(csB, 32, kWave);
+            if (hf == 0 && key < L && jA + 1 < G) s_h[(size_t)(g * G + jA + 1) * L + key] = (float)bsum;
+          }
+          csA = 0.0;
+          csB = 0.0;
+        }
+      }
+    }
+  }
+}
+
+// recent-query rows per head in the matrix-core path: 16 when q <= 16, else q rounded up to 32
+static int score_qp(int q) { return q <= 16 ? 16 : (q + 31) / 32 * 32; }
+
+int score_rows_padded(int Hq, int Hkv, int q) { return ((Hq / Hkv) * score_qp(q) + 31) / 32 * 32; }
 
 static bool use_mfma(int dtype, int Hq, int Hkv, int q) {
   return dtype == 1 && score_rows_padded(Hq, Hkv, q) <= kMRows;
 }
 
+// dynamic LDS of the two kernels for Rp rows of head dimension D (pass 1 is the larger)
+static size_t score_mfma_smem(int Rp, int D) { return (size_t)Rp * D * 2 + (size_t)Rp * 4 * (8 + 4); }
+
 template <int D>
 static hipError_t run_score_mfma(const void* Q, const void* K, int64_t L, int Hq, int Hkv, int q, float* s_h,
                                  double2* part, double2* rowstat, hipStream_t st) {
-  const int qp = (q + 15) / 16 * 16, Rp = score_rows_padded(Hq, Hkv, q);
+  const int qp = score_qp(q), Rp = score_rows_padded(Hq, Hkv, q);
   const double scale = 1.0 / sqrt((double)D), c = scale * 1.4426950408889634;
   // keys per block: 1024 when that still gives ~2 blocks per CU, down to 256 for short sequences
   int nsub = 4;
@@ -368,18 +426,18 @@ static hipError_t run_score_mfma(const void* Q, const void* K, int64_t L, int Hq
   const uint16_t* Qt = static_cast<const uint16_t*>(Q);
   const uint16_t* Kt = static_cast<const uint16_t*>(K);
   const size_t smem = score_mfma_smem(Rp, D);
-  if (smem > 48 * 1024) {                     // up to 79 KB for 256 rows: raise the dynamic-LDS limit
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel<D, 1>),
+  if (smem > 48 * 1024) {                     // up to 76 KB for 256 rows: raise the dynamic-LDS limit
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_p1_kernel<D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_mfma_kernel<D, 2>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_p2_kernel<D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  score_mfma_kernel<D, 1><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
+  score_p1_kernel<D><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part);
   const int64_t nrows = (int64_t)Hkv * Rp;
   score_combine_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(part, nrows, grid.x, scale, rowstat);
-  score_mfma_kernel<D, 2><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part, rowstat, s_h);
+  score_p2_kernel<D><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, rowstat, s_h);
   return hipGetLastError();
 }
 

@@ -22,8 +22,8 @@ constexpr int kRadixPasses = 4;
 // ---- score.hip ----------------------------------------------------------------------------------
 // Rows scored per KV group: R = (Hq/Hkv) * q; blocks of 256 keys; 4 waves per block.
 int64_t score_blocks(int64_t L);
-size_t score_partial_bytes(int64_t L, int Hq, int q);
-size_t score_rowstat_bytes(int Hq, int q);
+size_t score_partial_bytes(int64_t L, int Hq, int Hkv, int q);
+size_t score_rowstat_bytes(int Hq, int Hkv, int q);
 hipError_t launch_score(int dtype, int d, const void* Q, const void* K, int64_t L, int Hq, int Hkv,
                         int q, float* s_h, double2* partials, double2* rowstat, hipStream_t st);
 
