@@ -175,7 +175,7 @@ int tsa_dense_attn_causal(const tsa_shape* s, const void* Q, const void* K, cons
 int64_t tsa_block_count(int64_t L);
 /* Workspace of tsa_block_select and of tsa_layer_block_sparse.  tsa_block_select leaves the pooled
  * means in its workspace: qbar [Hq][NB][d] float32 at byte 0, kbar at the next multiple of 256
- * bytes after it. */
+ * bytes after it (then the float64 block logits [Hq][NB][NB]). */
 size_t tsa_block_select_workspace_bytes(const tsa_shape* s);
 size_t tsa_layer_block_sparse_workspace_bytes(const tsa_shape* s);
 

@@ -51,13 +51,14 @@ int64_t block_count(const tsa_shape* s) { return tsa_capacity(s->L) / kBlock; }
 size_t pooled_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * s->d * sizeof(float); }
 size_t list_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * block_count(s) * sizeof(uint16_t); }
 size_t count_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * sizeof(int32_t); }
+size_t logits_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * block_count(s) * sizeof(double); }
 
 // The layer workspace = stage workspace + every intermediate tensor of the layer (+ the block
 // lists of the block-sparse variant).
 struct LayerWs {
   StageWs st;
   size_t s_h, s_l, idx, inv, Qh, Kh, Vht, Oh, total;
-  size_t qbar, kbar, blist, bcnt, total_bs;
+  size_t qbar, kbar, zl, blist, bcnt, total_bs;
 };
 
 LayerWs layer_layout(const tsa_shape* s) {
@@ -79,6 +80,7 @@ LayerWs layer_layout(const tsa_shape* s) {
   w.total = o;
   w.qbar = take(pooled_bytes(s));
   w.kbar = take(pooled_bytes(s));
+  w.zl = take(logits_bytes(s));
   w.blist = take(list_bytes(s));
   w.bcnt = take(count_bytes(s));
   w.total_bs = o;
@@ -252,8 +254,8 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   if (block_sparse) {
     if (e == hipSuccess)
       e = launch_block_select(s->dtype, s->d, at<void>(ws, w.Qh), at<void>(ws, w.Kh), kLp + 1, C, s->Hq, (double)gamma,
-                              at<float>(ws, w.qbar), at<float>(ws, w.kbar), at<uint16_t>(ws, w.blist),
-                              at<int32_t>(ws, w.bcnt), st);
+                              at<float>(ws, w.qbar), at<float>(ws, w.kbar), at<double>(ws, w.zl),
+                              at<uint16_t>(ws, w.blist), at<int32_t>(ws, w.bcnt), st);
     if (e == hipSuccess)
       e = launch_attention_block_sparse(s->dtype, s->d, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
                                         kLp + 1, s->L, s->Hq, s->Hkv, C, at<uint16_t>(ws, w.blist),
@@ -550,7 +552,7 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
 int64_t tsa_block_count(int64_t L) { return tsa_capacity(L) / kBlock; }
 
 size_t tsa_block_select_workspace_bytes(const tsa_shape* s) {
-  return tsa_check_args(s) == TSA_OK ? 2 * up(pooled_bytes(s)) : 0;
+  return tsa_check_args(s) == TSA_OK ? 2 * up(pooled_bytes(s)) + up(logits_bytes(s)) : 0;
 }
 
 size_t tsa_layer_block_sparse_workspace_bytes(const tsa_shape* s) {
@@ -567,8 +569,9 @@ int tsa_block_select(const tsa_shape* s, float gamma, const void* Qh, const void
   TSA_TRY(check_ws(ws, ws_bytes, tsa_block_select_workspace_bytes(s)));
   float* qbar = at<float>(ws, 0);
   float* kbar = at<float>(ws, up(pooled_bytes(s)));
+  double* zl = at<double>(ws, 2 * up(pooled_bytes(s)));
   return hip_status(launch_block_select(s->dtype, s->d, Qh, Kh, Lp_dev, tsa_capacity(s->L), s->Hq, (double)gamma,
-                                        qbar, kbar, list, count, stream_of(stream)));
+                                        qbar, kbar, zl, list, count, stream_of(stream)));
 }
 
 int tsa_attn_block_sparse(const tsa_shape* s, const void* Qh, const void* Kh, const void* Vht, const int32_t* Lp_dev,

@@ -6,8 +6,9 @@
 //
 //   pool   : the rows of every block of kBlock compressed rows are averaged (float64 sum in row
 //            order, one division, rounded once to float32) into qbar, kbar [Hq][NB][d];
-//   select : query block I weighs its causal key blocks J <= I by a_J = softmax_J(<qbar_I, kbar_J>
-//            / sqrt(d)) (float64) and keeps the fewest heaviest (ties: lower J) whose weight reaches
+//   logits : zl[h][I][J] = <qbar_I, kbar_J> / sqrt(d) for J <= I, a tiled float64 product;
+//   select : query block I weighs its causal key blocks J <= I by a_J = softmax_J(zl[h][I][J])
+//            (float64) and keeps the fewest heaviest (ties: lower J) whose weight reaches
 //            gamma (all of them when gamma >= 1 or no prefix does), plus J = 0 and J = I.  The kept
 //            blocks are listed ascending: list [Hq][NB][NB] (uint16), count [Hq][NB].
 //
@@ -44,18 +45,62 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ Q
   (isk ? kbar : qbar)[((size_t)h * nbmax + b) * D + c] = (float)(acc / (double)(r1 - r0));
 }
 
+// zl[h][I][J] = <qbar[h][I], kbar[h][J]> / sqrt(d) for J <= I (float64 sums of exact float32
+// products), one 64 x 64 tile of (I, J) per workgroup: the pooled rows are read once per tile
+// instead of once per query block.  Each thread owns a 4 x 4 patch.
+template <int D>
+__global__ __launch_bounds__(256) void block_logits_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
+                                                           const int32_t* __restrict__ Lp_dev, int nbmax,
+                                                           double* __restrict__ zl) {
+  constexpr int T = 64, KC = 32;                 // tile edge, head-dim chunk staged at a time
+  __shared__ float qs[T][KC + 1], ks[T][KC + 1];
+  const int h = blockIdx.z, I0 = blockIdx.y * T, J0 = blockIdx.x * T;
+  const int nb = (int)((Lp_dev[0] + kBlock - 1) / kBlock);
+  if (J0 > I0 || I0 >= nb) return;               // causal tiles only
+  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < D; k0 += KC) {
+    for (int e = tid; e < T * KC; e += 256) {
+      const int r = e / KC, cc = e % KC;
+      qs[r][cc] = I0 + r < nb ? qbar[((size_t)h * nbmax + I0 + r) * D + k0 + cc] : 0.f;
+      ks[r][cc] = J0 + r < nb ? kbar[((size_t)h * nbmax + J0 + r) * D + k0 + cc] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int cc = 0; cc < KC; ++cc) {
+      double a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = (double)qs[ti + 16 * u][cc];
+        b[u] = (double)ks[tj + 16 * u][cc];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fma(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+  const double rsd = sqrt((double)D);
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int I = I0 + ti + 16 * u, J = J0 + tj + 16 * v;
+      if (I < nb && J <= I) zl[((size_t)h * nbmax + I) * nbmax + J] = acc[u][v] / rsd;
+    }
+}
+
 // "x comes before y": heavier first, then lower block index
 __device__ __forceinline__ bool before(double ax, int jx, double ay, int jy) {
   return ax > ay || (ax == ay && jx < jy);
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void block_select_kernel(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                           const int32_t* __restrict__ Lp_dev, int nbmax, double gamma,
-                                                           uint16_t* __restrict__ list, int32_t* __restrict__ count) {
+__global__ __launch_bounds__(256) void block_select_kernel(const double* __restrict__ zl, const int32_t* __restrict__ Lp_dev,
+                                                           int nbmax, double gamma, uint16_t* __restrict__ list,
+                                                           int32_t* __restrict__ count) {
   __shared__ double av[kSortMax];
   __shared__ uint16_t jv[kSortMax];
-  __shared__ float qb[D];
   __shared__ double red[4];
   __shared__ uint32_t kept[kSortMax / 32];
   __shared__ uint32_t wbase[kSortMax / 32];
@@ -71,20 +116,15 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
   const int n = I + 1;
   int P2 = 1;
   while (P2 < n) P2 <<= 1;
-  for (int c = tid; c < D; c += 256) qb[c] = qbar[((size_t)h * nbmax + I) * D + c];
   for (int i = tid; i < kSortMax / 32; i += 256) kept[i] = 0;
   if (tid == 0) cut = n - 1;
   __syncthreads();
 
-  // logits, max
-  const double rsd = sqrt((double)D);
+  // logits (block_logits_kernel), max
+  const double* zrow = zl + ((size_t)h * nbmax + I) * nbmax;
   double mx = -INFINITY;
   for (int J = tid; J < n; J += 256) {
-    const float* kr = kbar + ((size_t)h * nbmax + J) * D;
-    double z = 0.0;
-#pragma unroll 8
-    for (int c = 0; c < D; ++c) z += (double)qb[c] * (double)kr[c];
-    z /= rsd;
+    const double z = zrow[J];
     av[J] = z;
     mx = fmax(mx, z);
   }
@@ -187,8 +227,8 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
 }
 
 hipError_t launch_block_select(int dtype, int d, const void* Qh, const void* Kh, const int32_t* Lp_dev, int64_t C,
-                               int Hq, double gamma, float* qbar, float* kbar, uint16_t* list, int32_t* count,
-                               hipStream_t st) {
+                               int Hq, double gamma, float* qbar, float* kbar, double* zl, uint16_t* list,
+                               int32_t* count, hipStream_t st) {
   const int nbmax = (int)(C / kBlock);
   const dim3 grid((unsigned)nbmax, (unsigned)Hq);
   if (dtype == 1) {
@@ -206,10 +246,13 @@ hipError_t launch_block_select(int dtype, int d, const void* Qh, const void* Kh,
       block_pool_kernel<float, 64><<<grid, 256, 0, st>>>(static_cast<const float*>(Qh), static_cast<const float*>(Kh),
                                                          Lp_dev, C, nbmax, qbar, kbar);
   }
+  const unsigned nt = (unsigned)((nbmax + 63) / 64);
+  const dim3 lgrid(nt, nt, (unsigned)Hq);
   if (d == 128)
-    block_select_kernel<128><<<grid, 256, 0, st>>>(qbar, kbar, Lp_dev, nbmax, gamma, list, count);
+    block_logits_kernel<128><<<lgrid, 256, 0, st>>>(qbar, kbar, Lp_dev, nbmax, zl);
   else
-    block_select_kernel<64><<<grid, 256, 0, st>>>(qbar, kbar, Lp_dev, nbmax, gamma, list, count);
+    block_logits_kernel<64><<<lgrid, 256, 0, st>>>(qbar, kbar, Lp_dev, nbmax, zl);
+  block_select_kernel<<<grid, 256, 0, st>>>(zl, Lp_dev, nbmax, gamma, list, count);
   return hipGetLastError();
 }
 

@@ -63,11 +63,12 @@ hipError_t launch_scatter(int dtype, int d, const void* Oh, const int32_t* idx, 
 // kMaxKeyBlocks blocks per head (capacity <= kBlock * kMaxKeyBlocks rows).
 constexpr int kBlock = 128;
 constexpr int kMaxKeyBlocks = 4096;
-// Pools Qh/Kh [Hq][C][d] into qbar/kbar [Hq][C/kBlock][d] (float32) and writes the kept key blocks
-// of every query block: list [Hq][NB][NB] ascending, count [Hq][NB] (0 past the last block).
+// Pools Qh/Kh [Hq][C][d] into qbar/kbar [Hq][NB][d] (float32, NB = C/kBlock), forms the block
+// logits zl [Hq][NB][NB] (float64, causal half) and writes the kept key blocks of every query
+// block: list [Hq][NB][NB] ascending, count [Hq][NB] (0 past the last block).
 hipError_t launch_block_select(int dtype, int d, const void* Qh, const void* Kh, const int32_t* Lp_dev, int64_t C,
-                               int Hq, double gamma, float* qbar, float* kbar, uint16_t* list, int32_t* count,
-                               hipStream_t st);
+                               int Hq, double gamma, float* qbar, float* kbar, double* zl, uint16_t* list,
+                               int32_t* count, hipStream_t st);
 
 // ---- attention.hip ------------------------------------------------------------------------------
 // Compressed (dense == false): Qh/Kh [Hq][C][d], Vht [Hq][d][C], L' from Lp_dev, output Oh.
