@@ -45,7 +45,7 @@ extern "C" {
 typedef enum {
     TSA_OK = 0,
     TSA_ERR_ARG = 1,          /* NULL where a pointer is required, tau outside [0, 1), bad enum */
-    TSA_ERR_SHAPE = 2,        /* L, Hq, Hkv, d or q outside the supported ranges */
+    TSA_ERR_SHAPE = 2,        /* L, Hq, Hkv, d or q outside the supported ranges (L <= 2^24) */
     TSA_ERR_DTYPE = 3,        /* dtype is neither TSA_F32 nor TSA_BF16 */
     TSA_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
     TSA_ERR_WORKSPACE = 5,    /* workspace NULL, misaligned (256 B) or smaller than required */
@@ -55,7 +55,7 @@ typedef enum {
 
 typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
 
-/* Problem description.  Constraints: 1 <= q <= min(L, 1024); L < 2^31; 1 <= Hkv <= Hq <= 1024;
+/* Problem description.  Constraints: 1 <= q <= min(L, 1024); L <= 2^24; 1 <= Hkv <= Hq <= 1024;
  * Hq % Hkv == 0; d in {64, 128}; 0 <= tau < 1 (NaN rejected); dtype TSA_F32 or TSA_BF16. */
 typedef struct {
     int64_t L;       /* tokens */

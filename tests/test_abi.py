@@ -35,13 +35,19 @@ def good():
 
 @pytest.mark.parametrize("field,value,status", [
     ("dtype", 7, 3), ("tau", -0.1, 1), ("tau", 1.0, 1), ("tau", math.nan, 1),
-    ("L", 0, 2), ("L", 1 << 31, 2), ("Hq", 0, 2), ("Hkv", 3, 2), ("Hkv", 64, 2), ("q", 0, 2),
+    ("L", 0, 2), ("L", 1 << 31, 2), ("L", (1 << 24) + 1, 2), ("Hq", 0, 2), ("Hkv", 3, 2), ("Hkv", 64, 2), ("q", 0, 2),
     ("q", 4097, 2), ("q", 2000, 2), ("d", 96, 7), ("d", 256, 7),
 ])
 def test_check_args_rejects(field, value, status):
     s = good()
     setattr(s, field, value)
     assert binding.check_args(s) == status
+
+
+def test_check_args_length_limit():
+    s = good()
+    s.L = 1 << 24                         # the largest length the 32-bit buffer offsets allow
+    assert binding.check_args(s) == 0
 
 
 def test_check_args_accepts_the_workloads():

@@ -291,7 +291,9 @@ int tsa_check_args(const tsa_shape* s) {
   if (s == nullptr) return TSA_ERR_ARG;
   if (s->dtype != TSA_F32 && s->dtype != TSA_BF16) return TSA_ERR_DTYPE;
   if (!(s->tau >= 0.f && s->tau < 1.f)) return TSA_ERR_ARG;   // also rejects NaN
-  if (s->L < 1 || s->L >= (int64_t(1) << 31)) return TSA_ERR_SHAPE;
+  // L <= 2^24: the attention kernels address a transposed value row of C tokens through 32-bit
+  // buffer offsets ((d - 1) * 2C + 128 bytes must stay below 2^32)
+  if (s->L < 1 || s->L > (int64_t(1) << 24)) return TSA_ERR_SHAPE;
   if (s->Hq < 1 || s->Hkv < 1 || s->Hq > 1024 || s->Hkv > s->Hq || s->Hq % s->Hkv != 0) return TSA_ERR_SHAPE;
   if (s->q < 1 || s->q > 1024 || (int64_t)s->q > s->L) return TSA_ERR_SHAPE;
   if (s->d != 64 && s->d != 128) return TSA_ERR_UNSUPPORTED;

@@ -184,54 +184,51 @@ __device__ __forceinline__ uint4 add_vec(uint4 x, uint4 o) {
   return y;
 }
 
-// Token-major pass over Y using the inverse map: every (t, h) row is produced exactly once.
+// Pass over Y using the inverse map: every (t, h) row is produced exactly once.  Grid (token tiles,
+// heads); VPR threads cover one 16-byte-vector row, so no index division is needed.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ Oh, const int32_t* __restrict__ inv,
                                                           const T* X, T* Y, int64_t L, int Hq, int64_t C) {
   constexpr int VPR = D * (int)sizeof(T) / 16;
+  constexpr int TPB = 256 / VPR;                  // tokens per block
+  const int h = blockIdx.y, c = threadIdx.x % VPR;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / VPR;
+  if (t >= L) return;
   const uint4* O4 = reinterpret_cast<const uint4*>(Oh);
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
   uint4* Y4 = reinterpret_cast<uint4*>(Y);
-  const bool alias = (const void*)X == (const void*)Y;
-  const size_t n = (size_t)L * Hq * VPR;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    const size_t th = e / VPR;
-    const int c = (int)(e % VPR);
-    const int h = (int)(th % Hq);
-    const int64_t t = (int64_t)(th / Hq);
-    const int32_t j = inv[(size_t)h * L + t];
-    if (j < 0) {
-      if (alias) continue;
-      Y4[e] = X4 ? X4[e] : make_uint4(0, 0, 0, 0);
-    } else {
-      const uint4 o = O4[((size_t)h * C + j) * VPR + c];
-      Y4[e] = X4 ? add_vec<T>(X4[e], o) : o;
-    }
+  const size_t e = ((size_t)t * Hq + h) * VPR + c;
+  const int32_t j = inv[(size_t)h * L + t];
+  if (j < 0) {
+    if ((const void*)X == (const void*)Y) return;   // in place: the row already holds X
+    Y4[e] = X4 ? X4[e] : make_uint4(0, 0, 0, 0);
+  } else {
+    const uint4 o = O4[((size_t)h * C + j) * VPR + c];
+    Y4[e] = X4 ? add_vec<T>(X4[e], o) : o;
   }
 }
 
 // The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
-// One (token, head) pair per thread: the inverse map is read once and only unselected rows move.
+// Grid (token tiles, heads): the inverse map is read once per (token, head), coalesced along tokens,
+// and only unselected rows move.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fill_unselected_kernel(const int32_t* __restrict__ inv, const T* __restrict__ X,
                                                               T* __restrict__ Y, int64_t L, int Hq) {
   constexpr int VPR = D * (int)sizeof(T) / 16;
+  const int h = blockIdx.y;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= L || inv[(size_t)h * L + t] >= 0) return;
+  const size_t row = (size_t)t * Hq + h;
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
   uint4* Y4 = reinterpret_cast<uint4*>(Y);
-  const size_t n = (size_t)L * Hq;
-  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (size_t)gridDim.x * 256) {
-    if (inv[e] >= 0) continue;              // inv is [Hq][L]: consecutive threads, consecutive tokens
-    const size_t row = (size_t)(e % L) * Hq + e / L;
 #pragma unroll 4
-    for (int c = 0; c < VPR; ++c) Y4[row * VPR + c] = X4 ? X4[row * VPR + c] : make_uint4(0, 0, 0, 0);
-  }
+  for (int c = 0; c < VPR; ++c) Y4[row * VPR + c] = X4 ? X4[row * VPR + c] : make_uint4(0, 0, 0, 0);
 }
 
 template <typename T, int D>
 static hipError_t run_fill_unselected(const int32_t* inv, const void* X, void* Y, int64_t L, int Hq, hipStream_t st) {
-  const size_t n = (size_t)L * Hq;
-  const unsigned blocks = (unsigned)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
-  fill_unselected_kernel<T, D><<<blocks, 256, 0, st>>>(inv, static_cast<const T*>(X), static_cast<T*>(Y), L, Hq);
+  const dim3 grid((unsigned)((L + 255) / 256), (unsigned)Hq);
+  fill_unselected_kernel<T, D><<<grid, 256, 0, st>>>(inv, static_cast<const T*>(X), static_cast<T*>(Y), L, Hq);
   return hipGetLastError();
 }
 
@@ -331,8 +328,10 @@ static hipError_t run_scatter(const void* Oh, const int32_t* idx, const int32_t*
   constexpr int VPR = D * (int)sizeof(T) / 16;
   const size_t n = (size_t)L * Hq * VPR;
   if (inv) {
-    scatter_inv_kernel<T, D><<<grid_for(n), 256, 0, st>>>(static_cast<const T*>(Oh), inv,
-                                                          static_cast<const T*>(X), static_cast<T*>(Y), L, Hq, C);
+    constexpr int TPB = 256 / VPR;
+    const dim3 grid((unsigned)((L + TPB - 1) / TPB), (unsigned)Hq);
+    scatter_inv_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(Oh), inv, static_cast<const T*>(X),
+                                                   static_cast<T*>(Y), L, Hq, C);
     return hipGetLastError();
   }
   if (X == nullptr) {
