@@ -44,6 +44,24 @@ def timed(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
+def timed_cold(fn, steps, warmup, stream, flush):
+    """Median ms of fn() over `steps` calls, each after writing a 512 MiB scratch buffer so the
+    256 MB last-level cache holds none of fn's inputs; HIP events around each call."""
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(steps):
+        flush.fill_(1)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    return float(np.median(times))
+
+
 def algorithmic(cfg, Lp, union_rows):
     """Bytes (or flops) each stage must move (or compute) by definition, independent of how."""
     e = 2 if cfg.dtype == "bf16" else 4
@@ -338,13 +356,19 @@ def main():
     Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
     Oh = torch.empty_like(Qh)
     Ys = torch.empty_like(X)
+    # memory-bound stages: median of cold-cache calls (512 MiB written before each); attention:
+    # steady state, like the layer
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     st = {}
-    st["score"] = timed(lambda: binding.score(s, Q, K, s_h, s_l, sws), args.steps, 1, stream)
-    st["budget"] = timed(lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws), args.steps, 1, stream)
-    st["select"] = timed(lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws), args.steps, 1, stream)
-    st["gather"] = timed(lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht), args.steps, 1, stream)
+    st["score"] = timed_cold(lambda: binding.score(s, Q, K, s_h, s_l, sws), args.steps, 1, stream, flush)
+    st["budget"] = timed_cold(lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws), args.steps, 1, stream, flush)
+    st["select"] = timed_cold(lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws), args.steps, 1, stream, flush)
+    st["gather"] = timed_cold(lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht), args.steps, 1, stream,
+                              flush)
     st["attention"] = timed(lambda: binding.attn_causal(s, Qh, Kh, Vht, kl[1:2], Oh), args.steps, 1, stream)
-    st["scatter"] = timed(lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Ys), args.steps, 1, stream)
+    st["scatter"] = timed_cold(lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Ys), args.steps, 1,
+                               stream, flush)
+    del flush
     assert kl.tolist() == [k, Lp]
     # rows of K/V actually read by the gather: the union of the selections of each KV group
     G = cfg.Hq // cfg.Hkv
