@@ -44,6 +44,26 @@ def timed(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
+def timed_pair(fa, fb, steps, warmup, stream):
+    """Mean ms per call of fa() and of fb(), alternating a, b, a, b, ... so that clock drift over the
+    run affects both alike; every call is bracketed by synchronizations and HIP events."""
+    for _ in range(warmup):
+        fa()
+        fb()
+    ta, tb = [], []
+    for _ in range(steps):
+        for fn, acc in ((fa, ta), (fb, tb)):
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record(stream)
+            fn()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            acc.append(t0.elapsed_time(t1))
+    return float(np.mean(ta)), float(np.mean(tb))
+
+
 def timed_cold(fn, steps, warmup, stream, flush):
     """Median ms of fn() over `steps` calls, each after writing a 512 MiB scratch buffer so the
     256 MB last-level cache holds none of fn's inputs; HIP events around each call."""
@@ -331,17 +351,16 @@ def main():
     C = binding.capacity(cfg.L)
     stream = torch.cuda.current_stream()
 
-    # -- the whole layer --------------------------------------------------------------------------
+    # -- the whole layer and the dense baseline, alternating step by step ------------------------
     ws = binding.workspace(binding.layer_workspace_bytes(s), dev)
     kLp = torch.zeros(2, dtype=torch.int32, device=dev)
     Y = torch.empty_like(X)
-    layer_ms = timed(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws), args.steps, args.warmup, stream)
-    k, Lp = kLp.tolist()
-
-    # -- the dense baseline -----------------------------------------------------------------------
     dws = binding.workspace(binding.dense_workspace_bytes(s), dev)
     Yd = torch.empty_like(X)
-    dense_ms = timed(lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws), args.steps, args.warmup, stream)
+    layer_ms, dense_ms = timed_pair(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws),
+                                    lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws),
+                                    args.steps, args.warmup, stream)
+    k, Lp = kLp.tolist()
     del dws, Yd
 
     # -- stage by stage (same kernels, separate buffers) --------------------------------------------

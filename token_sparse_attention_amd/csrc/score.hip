@@ -349,12 +349,15 @@ __global__ __launch_bounds__(256, 2) void score_p2_kernel(const uint16_t* __rest
   __syncthreads();
 
   const int64_t bkeys = (int64_t)nsub * kMSub;
-  const bool open = (int64_t)(blockIdx.x + 1) * bkeys <= L - q + 1;
+  // key chunks in reverse order: pass 1 streamed K front to back, so its tail is what the
+  // last-level cache still holds
+  const int64_t kblk = (int64_t)gridDim.x - 1 - blockIdx.x;
+  const bool open = (kblk + 1) * bkeys <= L - q + 1;
   for (int sub = 0; sub < nsub; ++sub) {
 #pragma unroll 1
     for (int kb = 0; kb < 2; ++kb) {
       // this lane's key and its fragments (one block of 32 keys at a time keeps registers low)
-      const int64_t key = (int64_t)blockIdx.x * bkeys + sub * kMSub + 64 * w + 32 * kb + l32;
+      const int64_t key = kblk * bkeys + sub * kMSub + 64 * w + 32 * kb + l32;
       bf16x8s_t kf[KST];
 #pragma unroll
       for (int ks = 0; ks < KST; ++ks)
