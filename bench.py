@@ -44,6 +44,41 @@ def timed(fn, steps, warmup, stream):
     return t0.elapsed_time(t1) / steps
 
 
+def gpu_clocks():
+    """Shader clock, memory clock and power lines as rocm-smi prints them, or None when the tool is
+    unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    keep = [" ".join(ln.split()) for ln in r.stdout.splitlines()
+            if any(k in ln for k in ("sclk", "mclk", "Power (W)", "Power:")) and ln.strip()]
+    return keep or None
+
+
+class ClockSampler:
+    """Reads gpu_clocks() once, `delay` seconds after start(), from a background thread (the
+    sample then falls inside a timed region that lasts longer than the delay)."""
+
+    def __init__(self, delay):
+        import threading
+        self.delay, self.value = delay, None
+        self.thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        time.sleep(self.delay)
+        self.value = gpu_clocks()
+
+    def start(self):
+        self.thread.start()
+        return self
+
+    def result(self):
+        self.thread.join(timeout=30)
+        return self.value
+
+
 def timed_pair(fa, fb, steps, warmup, stream):
     """Mean ms per call of fa() and of fb(), alternating a, b, a, b, ... so that clock drift over the
     run affects both alike; every call is bracketed by synchronizations and HIP events."""
@@ -357,9 +392,11 @@ def main():
     Y = torch.empty_like(X)
     dws = binding.workspace(binding.dense_workspace_bytes(s), dev)
     Yd = torch.empty_like(X)
+    sampler = ClockSampler(delay=1.0).start()     # the timed loop below runs for seconds
     layer_ms, dense_ms = timed_pair(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws),
                                     lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws),
                                     args.steps, args.warmup, stream)
+    clocks = sampler.result()
     k, Lp = kLp.tolist()
     del dws, Yd
 
@@ -445,6 +482,7 @@ def main():
     if not args.no_varlen:
         del Qh, Kh, Vht, Oh, Ys, ws, sws
         out["supplementary_varlen"] = varlen_batch(max(2, args.steps // 2), 1, stream, dev)
+    out["gpu_clocks_during_layer_and_dense"] = clocks
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, Lp)
     print(json.dumps(out), flush=True)

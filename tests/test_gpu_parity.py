@@ -251,6 +251,10 @@ def test_attention_on_oracle_sets(case):
     assert_close(got, want, case.cfg.dtype, "O_hat")
     if Lp:
         assert (got[:, 0] == ov[:, 0]).all()          # one visible key: weight exactly 1
+        # per-head relative Frobenius error, an informative aggregate beside the element-wise bar
+        rel = [np.linalg.norm(got[h] - want[h]) / np.linalg.norm(want[h]) for h in range(case.cfg.Hq)]
+        print(f"\n[{case.cfg.name}] O_hat relative Frobenius error per head: max {max(rel):.2e}", flush=True)
+        assert max(rel) < (1e-2 if case.cfg.dtype == "bf16" else 1e-5), rel
 
 
 # -- stage 5 --------------------------------------------------------------------------------------
