@@ -4,7 +4,7 @@
 // selected indices are ascending).  The same kernels run the dense full-length attention that the
 // sparse layers are measured against.
 //
-// bf16 path (gfx950 matrix cores).  A block owns 128 query rows of one head, 4 waves x 32 rows, and
+// bf16 path (gfx950 matrix cores).  A block owns 256 query rows of one head, 8 waves x 32 rows, and
 // walks 64-key tiles of K and V^T staged in LDS (double-buffered, one barrier per tile).  The scores
 // are formed transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows, B = Q rows), so each
 // lane holds 32 scores of ONE query row: the row max is a lane-local reduction plus one exchange
@@ -26,6 +26,10 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// waves (of 32 query rows each) per workgroup of the dense and compressed bf16 kernels: 8 (one
+// 512-thread workgroup per CU, still two waves per SIMD) so that every K/V tile brought into LDS
+// serves 256 query rows; the block-sparse variant keeps 4 (its key-block lists are per 128 rows)
+constexpr int kAttnWaves = 8;
 
 // One sequence of a launch.  A launch covers up to kMaxSeg sequences packed along the token
 // dimension (a varlen batch; a single sequence is the one-segment case), each with its own length
@@ -113,17 +117,19 @@ __host__ __device__ __forceinline__ void dma_1k(const void* base, uint32_t bytes
 #endif
 }
 
-template <int D, bool DENSE, bool SPARSE, bool FUSED>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int BM = 128, BN = 64;
+template <int D, bool DENSE, bool SPARSE, bool FUSED, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(!SPARSE || NW == 4, "block-sparse lists are per 128 query rows");
+  constexpr int NT = 64 * NW;           // threads
+  constexpr int BM = 32 * NW, BN = 64;
   constexpr int KS = D / 16;            // K-steps of 16 over the head dim (score product)
   constexpr int DT = D / 32;            // 32-row tiles of O^T over the head dim
   constexpr int KROW = D * 2;           // bytes per K row in LDS (no padding; XOR-swizzled)
   constexpr int KTILE = BN * KROW;
   constexpr int VROW = BN * 2;          // bytes per V^T row in LDS
   constexpr int VTILE = D * VROW;
-  constexpr int KDMA = KTILE / 1024 / 4;  // 1 KiB direct loads per wave per K tile
-  constexpr int VDMA = VTILE / 1024 / 4;
+  constexpr int KDMA = KTILE / 1024 / NW;  // 1 KiB direct loads per wave per K tile
+  constexpr int VDMA = VTILE / 1024 / NW;
   constexpr int NS = 2 * KS, NV = 4 * DT, PF = 3;
   // LDS: K slots 0,1 then V slots 0,1
   __shared__ __attribute__((aligned(1024))) char smem[2 * KTILE + 2 * VTILE];
@@ -168,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
   if constexpr (SPARSE) {
     const size_t row = (size_t)h * a.nbmax + mb;
     const int nlist = a.bcnt[row];
-    for (int i = threadIdx.x; i < nlist; i += 256) klist[i] = a.blist[row * a.nbmax + i];
+    for (int i = threadIdx.x; i < nlist; i += NT) klist[i] = a.blist[row * a.nbmax + i];
     nkb = 2 * (nlist - 1) + (kend - m0 + BN - 1) / BN;
     __syncthreads();
   }
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     if (kb + 1 < nkb) dma_v(ktile(kb + 1), P ^ 1);
     const int key0 = ktile(kb) * BN, nval = Lp - key0;
     if (nval < BN) {                    // last tile: zero the V^T columns at and beyond L'
-      for (int e = tid; e < D * (BN - nval); e += 256) {
+      for (int e = tid; e < D * (BN - nval); e += NT) {
         const int r = e / (BN - nval), col = nval + e % (BN - nval);
         *reinterpret_cast<uint16_t*>(const_cast<char*>(vslot) + r * VROW + (((col >> 3) ^ vswz(r)) << 4) + (col & 7) * 2) = 0;
       }
@@ -465,8 +471,9 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int D, bool DENSE, bool SPARSE = false, bool FUSED = false>
 static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st) {
+  constexpr int NW = SPARSE ? 4 : kAttnWaves;
   if (dtype == 1)
-    attn_bf16_kernel<D, DENSE, SPARSE, FUSED><<<(unsigned)nblocks, 256, 0, st>>>(a);
+    attn_bf16_kernel<D, DENSE, SPARSE, FUSED, NW><<<(unsigned)nblocks, 64 * NW, 0, st>>>(a);
   else if (!FUSED)
     attn_f32_kernel<D, DENSE, SPARSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
   else
@@ -477,7 +484,7 @@ static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_
 hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, const void* K, const void* Vt,
                                    int nseq, const AttnSeqDesc* seqs, int Hq, int Hkv, const void* X, void* O,
                                    hipStream_t st, bool fused) {
-  const int bm = dtype == 1 ? 128 : 64;        // query rows per block
+  const int bm = dtype == 1 ? 32 * kAttnWaves : 64;   // query rows per block
   AttnArgs a{};
   a.Q = Q; a.K = K; a.Vt = Vt; a.X = X; a.O = O;
   a.Hq = Hq; a.Hkv = Hkv; a.scale = (float)(1.0 / sqrt((double)d));
