@@ -195,10 +195,11 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(cfg):
     """HBM bytes per launch of the compressed attention from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE, each divided by the factor the same counter reads for a plain copy
-    of known size), or None when that summary is missing or the kernel source has changed since."""
+    of known size), or None when that summary is missing, was taken on another shape than `cfg`'s,
+    or the kernel source has changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -207,6 +208,8 @@ def measured_traffic():
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    if (kv.get("workload_L"), kv.get("workload_Hq"), kv.get("workload_d")) != (str(cfg.L), str(cfg.Hq), str(cfg.d)):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -469,7 +472,7 @@ def main():
         "stages": stages,
         "roofline": {"bound": "mfma", "kernel": "compressed causal attention (bf16)", "achieved": round(att_tf, 1),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic()},
+                     "traffic": measured_traffic(cfg)},
         "input_gen_s": round(t_gen, 1),
     }
     if not args.no_tau_sweep:
