@@ -27,6 +27,15 @@ from token_sparse_attention_amd.inputs import make_batch, make_layer  # noqa: E4
 METRIC = "TSA layer ms & speedup vs own dense attn at L=128K; MFMA util, HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector peak
+
+
+T_START = time.perf_counter()
+
+
+def progress(msg):
+    """One line on stderr per finished phase (stdout carries only the JSON record)."""
+    print(f"[bench {time.perf_counter() - T_START:7.1f} s] {msg}", file=sys.stderr, flush=True)
 
 
 def timed(fn, steps, warmup, stream):
@@ -80,8 +89,9 @@ class ClockSampler:
 
 
 def timed_pair(fa, fb, steps, warmup, stream):
-    """Mean ms per call of fa() and of fb(), alternating a, b, a, b, ... so that clock drift over the
-    run affects both alike; every call is bracketed by synchronizations and HIP events."""
+    """Per-call ms of fa() and of fb() over `steps` calls of each, alternating a, b, a, b, ... so that
+    clock drift over the run affects both alike; every call is bracketed by synchronizations and HIP
+    events on the launch stream."""
     for _ in range(warmup):
         fa()
         fb()
@@ -96,11 +106,11 @@ def timed_pair(fa, fb, steps, warmup, stream):
             t1.record(stream)
             torch.cuda.synchronize()
             acc.append(t0.elapsed_time(t1))
-    return float(np.mean(ta)), float(np.mean(tb))
+    return ta, tb
 
 
 def timed_cold(fn, steps, warmup, stream, flush):
-    """Median ms of fn() over `steps` calls, each after writing a 512 MiB scratch buffer so the
+    """Per-call ms of fn() over `steps` calls, each after writing a 512 MiB scratch buffer so the
     256 MB last-level cache holds none of fn's inputs; HIP events around each call."""
     for _ in range(warmup):
         fn()
@@ -114,7 +124,13 @@ def timed_cold(fn, steps, warmup, stream, flush):
         t1.record(stream)
         torch.cuda.synchronize()
         times.append(t0.elapsed_time(t1))
-    return float(np.median(times))
+    return times
+
+
+def pct(times):
+    """p10 / p50 / p90 of per-call ms."""
+    p10, p50, p90 = np.percentile(np.asarray(times, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
 
 
 def algorithmic(cfg, Lp, union_rows):
@@ -132,11 +148,15 @@ def algorithmic(cfg, Lp, union_rows):
     }
 
 
-def cpu_baseline(cfg, inp, Lp_gpu, budget_s=12.0):
+PARITY_TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}   # |gpu - ref| <= atol + rtol |ref|
+
+
+def cpu_baseline(cfg, inp, k_gpu, Lp_gpu, Y_gpu, idx_gpu, budget_s=12.0):
     """The CPU oracle (float64, as it stands) on a bounded sample of the same workload, scaled to
     one full layer: scoring, budget and selection run in full; gather + attention run on a sample of
     output rows of a few heads and are scaled by the exact causal pair count; decompress + residual
-    runs on a sample of rows and is scaled by the row count."""
+    runs on a sample of rows and is scaled by the row count.  Returns that timing and, from the same
+    oracle results, the parity verdict of the GPU run being reported."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -157,7 +177,7 @@ def cpu_baseline(cfg, inp, Lp_gpu, budget_s=12.0):
     heads = [0, cfg.Hq // 2 + 1]
     t0 = time.perf_counter()
     sampled_pairs, n_rows = 0.0, 0
-    per_head = {}
+    per_head, kept = {}, {h: [] for h in heads}
     while time.perf_counter() - t0 < budget_s:
         for h in heads:
             if h not in per_head:
@@ -165,7 +185,9 @@ def cpu_baseline(cfg, inp, Lp_gpu, budget_s=12.0):
                 per_head[h] = (Q[idx[h], h, :], K[idx[h], g, :], V[idx[h], g, :])
             rows = np.sort(rng.choice(Lp, 16, replace=False))
             qh, kh, vh = per_head[h]
-            oracle.attention_rows(qh, kh, vh, idx[h], rows)
+            o = oracle.attention_rows(qh, kh, vh, idx[h], rows)
+            if len(kept[h]) < 8:
+                kept[h].append((rows, o))
             sampled_pairs += float(np.sum(rows + 1))
             n_rows += len(rows)
     t_att = time.perf_counter() - t0
@@ -178,12 +200,62 @@ def cpu_baseline(cfg, inp, Lp_gpu, budget_s=12.0):
     oracle.residual(X[:n_dec], oracle.decompress(Oh, np.tile(np.arange(n_dec), (cfg.Hq, 1)), n_dec))
     t_sc = (time.perf_counter() - t0) * cfg.L / n_dec
     total_ms = 1e3 * (t_sel + t_att_full + t_sc)
-    return {"value": round(total_ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
+    base = {"value": round(total_ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
             "sample": (f"numpy float64 oracle on this workload: scoring, budget and selection in full "
                        f"({t_sel:.1f} s); gather+attention on {n_rows} random rows of {len(heads)} heads "
                        f"({t_att:.1f} s) scaled by causal pair count to {cfg.Hq} heads x L'={Lp}; "
                        f"decompress+residual on {n_dec} rows scaled to L={cfg.L}"),
             "oracle_k": int(k), "oracle_Lp": int(Lp), "gpu_Lp": int(Lp_gpu)}
+    par = parity_verdict(cfg, inp["X"], s_h, s_l, k, Lp, idx, kept, k_gpu, Lp_gpu, Y_gpu, idx_gpu)
+    return base, par
+
+
+def parity_verdict(cfg, X_stored, s_h, s_l, k, Lp, idx, kept, k_gpu, Lp_gpu, Y_gpu, idx_gpu):
+    """The reported GPU run against the oracle, with the acceptance rules of the parity tests:
+    k equal, or both sides of the coverage threshold within 1e-5 relative; per-head selections equal,
+    or differing only on scores within 1e-6 of the boundary; the layer output at the oracle's sampled
+    attention rows within the floating-point tolerance; tokens a head did not keep equal to X
+    bitwise."""
+    tau = float(np.float32(cfg.tau))
+    Cs = np.concatenate([[0.0], np.cumsum(np.sort(s_l))])
+    budget_ok = k == k_gpu or (Cs[k_gpu] >= tau * (1 - 1e-5) and (k_gpu == 0 or Cs[k_gpu - 1] < tau * (1 + 1e-5)))
+    out = {"k_oracle": int(k), "k_gpu": int(k_gpu), "budget_ok": bool(budget_ok)}
+    if Lp != Lp_gpu:
+        out.update({"selection_compared": False, "pass": bool(budget_ok)})
+        return out
+    gsel = idx_gpu[:, :Lp].cpu().numpy().astype(np.int64)
+    equal, in_band = 0, 0
+    for h in range(cfg.Hq):
+        if np.array_equal(gsel[h], idx[h]):
+            equal += 1
+            continue
+        diff = np.setxor1d(gsel[h], idx[h])
+        bnd = np.sort(s_h[h])[::-1][Lp - 1]
+        in_band += int((np.abs(s_h[h][diff] - bnd) <= 1e-6 * bnd).all())
+    atol, rtol = PARITY_TOL[cfg.dtype]
+    X64 = X_stored.double()
+    n_rows, worst, bad, unsel_ok = 0, 0.0, 0, True
+    for h, samples in kept.items():
+        if not np.array_equal(gsel[h], idx[h]):
+            continue
+        for rows, o in samples:
+            tok = idx[h][rows]
+            got = Y_gpu[torch.as_tensor(tok, device=Y_gpu.device), h].double().cpu().numpy()
+            ref = X64[torch.as_tensor(tok), h].numpy() + o
+            err = np.abs(got - ref)
+            worst = max(worst, float(err.max()))
+            bad += int((err > atol + rtol * np.abs(ref)).sum())
+            n_rows += len(rows)
+        dropped = np.setdiff1d(np.arange(cfg.L), idx[h])[:64]
+        if len(dropped):
+            t = torch.as_tensor(dropped)
+            unsel_ok &= bool(torch.equal(Y_gpu[t.to(Y_gpu.device), h].cpu(), X_stored[t, h]))
+    out.update({"selection_compared": True, "heads_selection_equal": equal, "heads_within_tie_band": in_band,
+                "output_rows_checked": n_rows, "output_max_abs_err": round(worst, 6),
+                "output_tolerance": f"{atol:g} + {rtol:g} |ref|", "output_outside_tolerance": bad,
+                "unselected_rows_equal_X": unsel_ok})
+    out["pass"] = bool(budget_ok and equal + in_band == cfg.Hq and bad == 0 and n_rows > 0 and unsel_ok)
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_attention_L131072_bf16.txt")
@@ -354,6 +426,84 @@ def varlen_batch(steps, warmup, stream, dev):
     return out
 
 
+def measure_workload(cfg, Q, K, V, X, steps, warmup, stream, sample_clocks=False):
+    """Everything timed on one workload with inputs resident in HBM: the whole layer and the dense
+    baseline alternately step by step, then every stage through its own ABI call (memory-bound
+    stages with a cold last-level cache, the attention in steady state).  Returns the record and
+    the tensors a later parity check needs (Y of the layer, the stage call's selection)."""
+    dev = Q.device
+    s = binding.shape_of(cfg)
+    C = binding.capacity(cfg.L)
+    ws = binding.workspace(binding.layer_workspace_bytes(s), dev)
+    kLp = torch.zeros(2, dtype=torch.int32, device=dev)
+    Y = torch.empty_like(X)
+    dws = binding.workspace(binding.dense_workspace_bytes(s), dev)
+    Yd = torch.empty_like(X)
+    sampler = ClockSampler(delay=1.0).start() if sample_clocks else None   # the loop runs for seconds
+    tl, td = timed_pair(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws),
+                        lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws), steps, warmup, stream)
+    clocks = sampler.result() if sampler else None
+    layer_ms, dense_ms = float(np.mean(tl)), float(np.mean(td))
+    k, Lp = kLp.tolist()
+    del dws, Yd, ws
+
+    sws = binding.workspace(binding.stage_workspace_bytes(s), dev)
+    s_h = torch.empty(cfg.Hq, cfg.L, dtype=torch.float32, device=dev)
+    s_l = torch.empty(cfg.L, dtype=torch.float32, device=dev)
+    kl = torch.zeros(2, dtype=torch.int32, device=dev)
+    idx = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
+    inv = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
+    Qh = torch.empty(cfg.Hq, C, cfg.d, dtype=Q.dtype, device=dev)
+    Kh = torch.empty_like(Qh)
+    Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
+    Oh = torch.empty_like(Qh)
+    Ys = torch.empty_like(X)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    calls = {}
+    calls["score"] = timed_cold(lambda: binding.score(s, Q, K, s_h, s_l, sws), steps, 1, stream, flush)
+    calls["budget"] = timed_cold(lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws), steps, 1, stream, flush)
+    calls["select"] = timed_cold(lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws), steps, 1, stream, flush)
+    calls["gather"] = timed_cold(lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht), steps, 1, stream,
+                                 flush)
+    att_ms = timed(lambda: binding.attn_causal(s, Qh, Kh, Vht, kl[1:2], Oh), steps, 1, stream)
+    calls["scatter"] = timed_cold(lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Ys), steps, 1,
+                                  stream, flush)
+    del flush, Qh, Kh, Vht, Oh, Ys, sws, inv
+    assert kl.tolist() == [k, Lp]
+    sl = s_l.double().cpu().numpy()
+    # rows of K/V actually read by the gather: the union of the selections of each KV group
+    G = cfg.Hq // cfg.Hkv
+    sel = idx[:, :Lp].cpu().numpy()
+    union_rows = sum(len(np.unique(sel[g * G:(g + 1) * G])) for g in range(cfg.Hkv))
+    alg = algorithmic(cfg, Lp, union_rows)
+
+    stages = {}
+    for name in ("score", "budget", "select", "gather", "scatter"):
+        ms = float(np.median(calls[name]))
+        rate = alg[name] / (ms * 1e-3) / 1e9
+        stages[name] = {"ms": round(ms, 4), "ms_percentiles": pct(calls[name]), "algorithmic_bytes": int(alg[name]),
+                        "GB_s": round(rate, 1), "hbm_frac": round(rate / HBM_PEAK_GBS, 4)}
+    peak = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
+    frac_key = "mfma_frac" if cfg.dtype == "bf16" else "fp32_vector_frac"
+    att_tf = alg["attn_flops"] / (att_ms * 1e-3) / 1e12
+    stages["attention"] = {"ms": round(att_ms, 4), "algorithmic_flops": int(alg["attn_flops"]),
+                           "TFLOP_s": round(att_tf, 1), frac_key: round(att_tf / peak, 4)}
+    dense_tf = alg["dense_flops"] / (dense_ms * 1e-3) / 1e12
+    rec = {
+        "workload": cfg.name, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d, "q": cfg.q, "tau": cfg.tau,
+        "dtype": cfg.dtype, "seed": cfg.seed, "k": k, "L_keep": Lp,
+        "s_l_min_times_L": round(float(sl.min()) * cfg.L, 4), "s_l_max_times_L": round(float(sl.max()) * cfg.L, 4),
+        "layer_ms": round(layer_ms, 4), "layer_ms_percentiles": pct(tl),
+        "dense_ms": round(dense_ms, 4), "dense_ms_percentiles": pct(td),
+        "speedup_vs_dense": round(dense_ms / layer_ms, 4),
+        "attention_only_speedup": round(dense_ms / att_ms, 4),
+        "dense_TFLOP_s": round(dense_tf, 1), "dense_" + frac_key: round(dense_tf / peak, 4),
+        "overhead_frac_of_attention": round((layer_ms - att_ms) / att_ms, 4),
+        "stages": stages,
+    }
+    return rec, {"Y": Y, "idx": idx, "k": k, "Lp": Lp, "clocks": clocks, "att_tf": att_tf, "peak": peak}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,6 +514,8 @@ def main():
     ap.add_argument("--no-tau-sweep", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-block-sparse", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload records of the other workloads")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the short kernel sequence used for the rocprofv3 counter passes")
     args = ap.parse_args()
@@ -385,69 +537,13 @@ def main():
     inp = make_layer(cfg)
     t_gen = time.perf_counter() - t_gen
     Q, K, V, X = (inp[n].to(dev) for n in ("Q", "K", "V", "X"))
-    s = binding.shape_of(cfg)
-    C = binding.capacity(cfg.L)
     stream = torch.cuda.current_stream()
 
-    # -- the whole layer and the dense baseline, alternating step by step ------------------------
-    ws = binding.workspace(binding.layer_workspace_bytes(s), dev)
-    kLp = torch.zeros(2, dtype=torch.int32, device=dev)
-    Y = torch.empty_like(X)
-    dws = binding.workspace(binding.dense_workspace_bytes(s), dev)
-    Yd = torch.empty_like(X)
-    sampler = ClockSampler(delay=1.0).start()     # the timed loop below runs for seconds
-    layer_ms, dense_ms = timed_pair(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws),
-                                    lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws),
-                                    args.steps, args.warmup, stream)
-    clocks = sampler.result()
-    k, Lp = kLp.tolist()
-    del dws, Yd
-
-    # -- stage by stage (same kernels, separate buffers) --------------------------------------------
-    sws = binding.workspace(binding.stage_workspace_bytes(s), dev)
-    s_h = torch.empty(cfg.Hq, cfg.L, dtype=torch.float32, device=dev)
-    s_l = torch.empty(cfg.L, dtype=torch.float32, device=dev)
-    kl = torch.zeros(2, dtype=torch.int32, device=dev)
-    idx = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
-    inv = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
-    Qh = torch.empty(cfg.Hq, C, cfg.d, dtype=Q.dtype, device=dev)
-    Kh = torch.empty_like(Qh)
-    Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
-    Oh = torch.empty_like(Qh)
-    Ys = torch.empty_like(X)
-    # memory-bound stages: median of cold-cache calls (512 MiB written before each); attention:
-    # steady state, like the layer
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    st = {}
-    st["score"] = timed_cold(lambda: binding.score(s, Q, K, s_h, s_l, sws), args.steps, 1, stream, flush)
-    st["budget"] = timed_cold(lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws), args.steps, 1, stream, flush)
-    st["select"] = timed_cold(lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws), args.steps, 1, stream, flush)
-    st["gather"] = timed_cold(lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht), args.steps, 1, stream,
-                              flush)
-    st["attention"] = timed(lambda: binding.attn_causal(s, Qh, Kh, Vht, kl[1:2], Oh), args.steps, 1, stream)
-    st["scatter"] = timed_cold(lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Ys), args.steps, 1,
-                               stream, flush)
-    del flush
-    assert kl.tolist() == [k, Lp]
-    # rows of K/V actually read by the gather: the union of the selections of each KV group
-    G = cfg.Hq // cfg.Hkv
-    sel = idx[:, :Lp].cpu().numpy()
-    union_rows = sum(len(np.unique(sel[g * G:(g + 1) * G])) for g in range(cfg.Hkv))
-    alg = algorithmic(cfg, Lp, union_rows)
-
-    def gbs(nbytes, ms):
-        return nbytes / (ms * 1e-3) / 1e9
-
-    stages = {}
-    for name in ("score", "budget", "select", "gather", "scatter"):
-        rate = gbs(alg[name], st[name])
-        stages[name] = {"ms": round(st[name], 4), "algorithmic_bytes": int(alg[name]), "GB_s": round(rate, 1),
-                        "hbm_frac": round(rate / HBM_PEAK_GBS, 4)}
-    att_tf = alg["attn_flops"] / (st["attention"] * 1e-3) / 1e12
-    stages["attention"] = {"ms": round(st["attention"], 4), "algorithmic_flops": int(alg["attn_flops"]),
-                           "TFLOP_s": round(att_tf, 1), "mfma_frac": round(att_tf / BF16_PEAK_TFLOPS, 4)}
-    dense_tf = alg["dense_flops"] / (dense_ms * 1e-3) / 1e12
-
+    progress(f"inputs of {cfg.name} drawn in {t_gen:.1f} s")
+    rec, keep = measure_workload(cfg, Q, K, V, X, args.steps, args.warmup, stream, sample_clocks=True)
+    progress(f"layer {rec['layer_ms']:.3f} ms, dense {rec['dense_ms']:.3f} ms, stages timed")
+    layer_ms, dense_ms = rec["layer_ms"], rec["dense_ms"]
+    frac_key = "mfma_frac" if cfg.dtype == "bf16" else "fp32_vector_frac"
     out = {
         "metric": METRIC,
         "value": round(layer_ms, 3),
@@ -462,32 +558,53 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": cfg.name, "L": cfg.L, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d, "q": cfg.q,
-                   "tau": cfg.tau, "seed": cfg.seed, "k": k, "L_keep": Lp, "parallelism": "single GPU"},
-        "dense_ms": round(dense_ms, 3),
-        "speedup_vs_dense": round(dense_ms / layer_ms, 4),
-        "attention_only_speedup": round(dense_ms / st["attention"], 4),
-        "dense_TFLOP_s": round(dense_tf, 1),
-        "dense_mfma_frac": round(dense_tf / BF16_PEAK_TFLOPS, 4),
-        "overhead_frac_of_attention": round((layer_ms - st["attention"]) / st["attention"], 4),
-        "stages": stages,
-        "roofline": {"bound": "mfma", "kernel": "compressed causal attention (bf16)", "achieved": round(att_tf, 1),
-                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(att_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(cfg)},
-        "input_gen_s": round(t_gen, 1),
+                   "tau": cfg.tau, "seed": cfg.seed, "k": keep["k"], "L_keep": keep["Lp"],
+                   "parallelism": "single GPU"},
     }
+    for key in ("layer_ms_percentiles", "dense_ms", "dense_ms_percentiles", "speedup_vs_dense",
+                "attention_only_speedup", "dense_TFLOP_s", "dense_" + frac_key, "overhead_frac_of_attention",
+                "s_l_min_times_L", "s_l_max_times_L", "stages"):
+        out[key] = rec[key]
+    out["roofline"] = {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
+                       "kernel": f"compressed causal attention ({cfg.dtype})",
+                       "achieved": round(keep["att_tf"], 1), "peak": keep["peak"], "unit": "TFLOP/s",
+                       "frac": round(keep["att_tf"] / keep["peak"], 4), "traffic": measured_traffic(cfg)}
+    out["input_gen_s"] = round(t_gen, 1)
+    sub = max(2, args.steps // 2)
     if not args.no_tau_sweep:
-        out["supplementary_tau_sweep"] = tau_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1, stream)
-        out["supplementary_fixed_ratio"] = ratio_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1,
-                                                       stream)
+        out["supplementary_tau_sweep"] = tau_sweep(cfg, Q, K, V, X, dense_ms, sub, 1, stream)
+        out["supplementary_fixed_ratio"] = ratio_sweep(cfg, Q, K, V, X, dense_ms, sub, 1, stream)
+        progress("tau sweep and fixed ratio done")
     if not args.no_block_sparse:
-        out["supplementary_block_sparse"] = block_sparse_sweep(cfg, Q, K, V, X, dense_ms, max(2, args.steps // 2), 1,
-                                                               stream)
-    if not args.no_varlen:
-        del Qh, Kh, Vht, Oh, Ys, ws, sws
-        out["supplementary_varlen"] = varlen_batch(max(2, args.steps // 2), 1, stream, dev)
-    out["gpu_clocks_during_layer_and_dense"] = clocks
+        out["supplementary_block_sparse"] = block_sparse_sweep(cfg, Q, K, V, X, dense_ms, sub, 1, stream)
+        progress("block sparsity done")
+    out["gpu_clocks_during_layer_and_dense"] = keep["clocks"]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, Lp)
+        Yc, idxc = keep["Y"], keep["idx"]
+        out["cpu_baseline"], out["parity_vs_oracle"] = cpu_baseline(cfg, inp, keep["k"], keep["Lp"], Yc, idxc)
+        progress(f"oracle timed; parity pass = {out['parity_vs_oracle']['pass']}")
+    del Q, K, V, X, inp, keep
+    torch.cuda.empty_cache()
+    if not args.no_varlen:
+        out["supplementary_varlen"] = varlen_batch(sub, 1, stream, dev)
+        progress("varlen batch done")
+    if not args.no_configs:
+        recs = []
+        for n in sorted(CONFIGS):
+            if n == args.workload:
+                continue
+            c = CONFIGS[n]
+            t0 = time.perf_counter()
+            part = make_layer(c)
+            Qc, Kc, Vc, Xc = (part[m].to(dev) for m in ("Q", "K", "V", "X"))
+            del part
+            r, _ = measure_workload(c, Qc, Kc, Vc, Xc, 3 if c.L > 131072 else sub, 1, stream)
+            r["wall_s"] = round(time.perf_counter() - t0, 1)
+            recs.append(r)
+            progress(f"{c.name}: layer {r['layer_ms']:.3f} ms, dense {r['dense_ms']:.3f} ms")
+            del Qc, Kc, Vc, Xc, _
+            torch.cuda.empty_cache()
+        out["supplementary_configs"] = recs
     print(json.dumps(out), flush=True)
 
 

@@ -1,12 +1,18 @@
 """Host-side rules of bench.py that need no GPU: the counter-derived traffic figure is reported only
-for the shape and kernel source it was measured on, and a multi-GPU request is refused."""
+for the shape and kernel source it was measured on, a multi-GPU request is refused, and the parity
+verdict attached to the CPU baseline accepts the oracle's own layer and rejects planted mistakes."""
 
 import os
 import subprocess
 import sys
 
+import numpy as np
+import torch
+
 import bench
+import oracle
 from token_sparse_attention_amd.configs import CONFIGS
+from token_sparse_attention_amd.inputs import make_layer
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -37,3 +43,55 @@ def test_multi_gpu_request_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _oracle_run(cfg):
+    """The oracle's own layer on a small workload, shaped like a device run (Y as stored, idx padded
+    to [Hq][L]), and the oracle's sampled attention rows as the CPU baseline keeps them."""
+    inp = make_layer(cfg)
+    f64 = lambda t: t.double().numpy()
+    Q, K, V, X = (f64(inp[n]) for n in ("Q", "K", "V", "X"))
+    r = oracle.layer(Q, K, V, X, float(np.float32(cfg.tau)), cfg.q)
+    Lp = r["Lp"]
+    Y = torch.from_numpy(r["Y"]).to(torch.float32)
+    idx = torch.full((cfg.Hq, cfg.L), -1, dtype=torch.int32)
+    idx[:, :Lp] = torch.from_numpy(np.asarray(r["idx"], dtype=np.int32))
+    rng = np.random.default_rng(1)
+    kept = {}
+    for h in (0, cfg.Hq - 1):
+        rows = np.sort(rng.choice(Lp, 16, replace=False))
+        kept[h] = [(rows, r["Oh"][h][rows])]
+    return inp, r, Y, idx, kept
+
+
+def test_parity_verdict_accepts_the_oracle_and_rejects_planted_errors():
+    cfg = CONFIGS[1]
+    inp, r, Y, idx, kept = _oracle_run(cfg)
+    k, Lp = r["k"], r["Lp"]
+    args = (cfg, inp["X"], r["s_h"], r["s_l"], k, Lp, r["idx"], kept)
+    ok = bench.parity_verdict(*args, k, Lp, Y, idx)
+    assert ok["pass"] and ok["heads_selection_equal"] == cfg.Hq and ok["output_rows_checked"] == 32
+    assert ok["unselected_rows_equal_X"] and ok["output_outside_tolerance"] == 0
+    # a wrong value at one sampled output row
+    rows, _ = kept[0][0]
+    Yb = Y.clone()
+    Yb[int(r["idx"][0][rows[3]]), 0, 5] += 0.01
+    bad = bench.parity_verdict(*args, k, Lp, Yb, idx)
+    assert not bad["pass"] and bad["output_outside_tolerance"] == 1
+    # a token a head did not keep must stay X
+    dropped = int(np.setdiff1d(np.arange(cfg.L), r["idx"][0])[0])
+    Yb = Y.clone()
+    Yb[dropped, 0, 0] += 1.0
+    assert not bench.parity_verdict(*args, k, Lp, Yb, idx)["unselected_rows_equal_X"]
+    # a selection that swaps a clearly kept token for a clearly dropped one
+    ib = idx.clone()
+    top = int(np.argmax(r["s_h"][1]))
+    low = int(np.argmin(r["s_h"][1]))
+    sel = set(r["idx"][1].tolist())
+    assert top in sel and low not in sel
+    sel = sorted((sel - {top}) | {low})
+    ib[1, :Lp] = torch.tensor(sel, dtype=torch.int32)
+    v = bench.parity_verdict(*args, k, Lp, Y, ib)
+    assert not v["pass"] and v["heads_selection_equal"] == cfg.Hq - 1 and v["heads_within_tie_band"] == 0
+    # a budget off by one is outside the coverage band
+    assert not bench.parity_verdict(*args, k + 1, Lp, Y, idx)["budget_ok"]
