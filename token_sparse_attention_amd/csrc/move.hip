@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
     if (r < n) {
       const int64_t t = idx[(size_t)h * L + i0 + r];
       const size_t dst = ((size_t)h * C + i0 + r) * VPR + c;
-      if (Qh4) Qh4[dst] = Q4[((size_t)t * Hq + h) * VPR + c];   // the fused layer reads Q in place
-      Kh4[dst] = K4[((size_t)t * Hkv + g) * VPR + c];
+      if (Qh4) st_stream(ld_stream(&Q4[((size_t)t * Hq + h) * VPR + c]), &Qh4[dst]);   // the fused layer reads Q in place
+      st_stream(K4[((size_t)t * Hkv + g) * VPR + c], &Kh4[dst]);
       v = V4[((size_t)t * Hkv + g) * VPR + c];
     }
     stage[e] = v;
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __rest
     if (i < Lp) {
       const int64_t t = idx[(size_t)h * L + i];
       const size_t dst = ((size_t)h * C + i) * VPR + c;
-      if (Qh4) Qh4[dst] = Q4[((size_t)t * Hq + h) * VPR + c];   // the fused layer reads Q in place
-      Kh4[dst] = K4[((size_t)t * Hkv + g) * VPR + c];
+      if (Qh4) st_stream(ld_stream(&Q4[((size_t)t * Hq + h) * VPR + c]), &Qh4[dst]);   // the fused layer reads Q in place
+      st_stream(K4[((size_t)t * Hkv + g) * VPR + c], &Kh4[dst]);
       x = V4[((size_t)t * Hkv + g) * VPR + c];
     }
     v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __rest
   for (int e = threadIdx.x; e < D * PPC; e += 256) {
     const int col = e / PPC, q = e % PPC;
     if ((int64_t)q * 8 >= nrows) continue;
-    *reinterpret_cast<uint4*>(Vht + ((size_t)h * D + col) * C + b0 + 8 * q) = tile[col * PPC + (q ^ (col % PPC))];
+    st_stream(tile[col * PPC + (q ^ (col % PPC))], reinterpret_cast<uint4*>(Vht + ((size_t)h * D + col) * C + b0 + 8 * q));
   }
 }
 
@@ -201,10 +201,10 @@ __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ 
   const int32_t j = inv[(size_t)h * L + t];
   if (j < 0) {
     if ((const void*)X == (const void*)Y) return;   // in place: the row already holds X
-    Y4[e] = X4 ? X4[e] : make_uint4(0, 0, 0, 0);
+    st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), &Y4[e]);
   } else {
-    const uint4 o = O4[((size_t)h * C + j) * VPR + c];
-    Y4[e] = X4 ? add_vec<T>(X4[e], o) : o;
+    const uint4 o = ld_stream(&O4[((size_t)h * C + j) * VPR + c]);
+    st_stream(X4 ? add_vec<T>(ld_stream(&X4[e]), o) : o, &Y4[e]);
   }
 }
 
@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256) void fill_unselected_kernel(const int32_t* __r
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
   uint4* Y4 = reinterpret_cast<uint4*>(Y);
 #pragma unroll 4
-  for (int c = 0; c < VPR; ++c) Y4[row * VPR + c] = X4 ? X4[row * VPR + c] : make_uint4(0, 0, 0, 0);
+  for (int c = 0; c < VPR; ++c) st_stream(X4 ? ld_stream(&X4[row * VPR + c]) : make_uint4(0, 0, 0, 0), &Y4[row * VPR + c]);
 }
 
 template <typename T, int D>
