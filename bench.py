@@ -133,6 +133,44 @@ def pct(times):
     return {"p10": round(float(p10), 4), "p50": round(float(p50), 4), "p90": round(float(p90), 4)}
 
 
+def hbm_practical(dev, steps=10):
+    """What plain torch device operations reach on this GPU, as context for the stage fractions
+    (all against the 8 TB/s published peak): a write-only fill and a copy of a 2 GiB buffer, median
+    of `steps` calls each."""
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.fill_(2)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    fill_ms = float(np.median(timed_calls(lambda: a.fill_(3), steps, 1, stream)))
+    copy_ms = float(np.median(timed_calls(lambda: b.copy_(a), steps, 1, stream)))
+    del a, b
+    torch.cuda.empty_cache()
+    fill, copy = n / (fill_ms * 1e-3) / 1e9, 2 * n / (copy_ms * 1e-3) / 1e9
+    return {"write_only_fill_GB_s": round(fill, 1), "fill_frac": round(fill / HBM_PEAK_GBS, 4),
+            "copy_GB_s": round(copy, 1), "copy_frac": round(copy / HBM_PEAK_GBS, 4),
+            "how": "torch fill_ and copy_ on 2 GiB device buffers, median of per-call HIP events"}
+
+
+def timed_calls(fn, steps, warmup, stream):
+    """Per-call ms of fn() in steady state (no cache flush), every call bracketed by HIP events."""
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(steps):
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        fn()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1))
+    return times
+
+
 def algorithmic(cfg, Lp, union_rows):
     """Bytes (or flops) each stage must move (or compute) by definition, independent of how."""
     e = 2 if cfg.dtype == "bf16" else 4
@@ -289,9 +327,16 @@ def measured_traffic(cfg):
         return None
 
 
+STAGE_SOURCES = {"score": "score.hip", "budget": "select.hip", "select": "select.hip", "gather": "move.hip",
+                 "scatter": "move.hip"}
+STAGE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stages_L131072_bf16.txt")
+
+
 def traffic_probe(cfg, dev):
     """A short run for the counter passes: three compressed-attention launches on this workload's
-    shape (L' = L, random bf16) and three copies of a 1 GiB buffer, the calibration of known size."""
+    shape (L' = L, random bf16) and three copies of a 1 GiB buffer (the calibration of known size),
+    then each memory-bound stage once through its own ABI call on this workload's inputs, after a
+    512 MiB write that evicts its inputs from the caches."""
     s = binding.shape_of(cfg)
     C = binding.capacity(cfg.L)
     g = torch.Generator(device=dev).manual_seed(0)
@@ -307,7 +352,50 @@ def traffic_probe(cfg, dev):
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"traffic_probe": cfg.name, "copy_bytes": 1 << 30, "attention_launches": 3}), flush=True)
+    del src, dst, Vht
+    inp = make_layer(cfg)
+    Q, K, V, X = (inp[n].to(dev) for n in ("Q", "K", "V", "X"))
+    del inp
+    sws = binding.workspace(binding.stage_workspace_bytes(s), dev)
+    s_h = torch.empty(cfg.Hq, cfg.L, dtype=torch.float32, device=dev)
+    s_l = torch.empty(cfg.L, dtype=torch.float32, device=dev)
+    kl = torch.zeros(2, dtype=torch.int32, device=dev)
+    idx = torch.empty(cfg.Hq, cfg.L, dtype=torch.int32, device=dev)
+    inv = torch.empty_like(idx)
+    Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
+    Y = torch.empty_like(X)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stages = [("score", lambda: binding.score(s, Q, K, s_h, s_l, sws)),
+              ("budget", lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws)),
+              ("select", lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws)),
+              ("gather", lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht)),
+              ("scatter", lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Y))]
+    for _, fn in stages:
+        flush.fill_(1)
+        fn()
+        torch.cuda.synchronize()
+    print(json.dumps({"traffic_probe": cfg.name, "copy_bytes": 1 << 30, "attention_launches": 3,
+                      "stages": [n for n, _ in stages], "k": int(kl[0]), "L_keep": int(kl[1])}), flush=True)
+
+
+def measured_stage_traffic(cfg):
+    """Counted HBM bytes per call of each memory-bound stage from the committed counter summary, for
+    the stages whose kernel source still hashes as it did when counted, on the counted shape only."""
+    if not os.path.exists(STAGE_TRAFFIC_FILE):
+        return {}
+    kv = {}
+    for line in open(STAGE_TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if (kv.get("workload_L"), kv.get("workload_Hq"), kv.get("workload_d")) != (str(cfg.L), str(cfg.Hq), str(cfg.d)):
+        return {}
+    out = {}
+    for st, src in STAGE_SOURCES.items():
+        h = source_hash(os.path.join(ROOT, "token_sparse_attention_amd", "csrc", src))
+        if kv.get(f"source_sha256_16 {src}") == h and f"{st}_hbm_bytes" in kv:
+            out[st] = int(float(kv[f"{st}_hbm_bytes"]))
+    return out
 
 
 def tau_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
@@ -565,6 +653,9 @@ def main():
                 "attention_only_speedup", "dense_TFLOP_s", "dense_" + frac_key, "overhead_frac_of_attention",
                 "s_l_min_times_L", "s_l_max_times_L", "stages"):
         out[key] = rec[key]
+    for st, nbytes in measured_stage_traffic(cfg).items():
+        out["stages"][st]["counted_hbm_bytes"] = nbytes
+        out["stages"][st]["counted_over_algorithmic"] = round(nbytes / out["stages"][st]["algorithmic_bytes"], 3)
     out["roofline"] = {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
                        "kernel": f"compressed causal attention ({cfg.dtype})",
                        "achieved": round(keep["att_tf"], 1), "peak": keep["peak"], "unit": "TFLOP/s",
@@ -579,6 +670,7 @@ def main():
         out["supplementary_block_sparse"] = block_sparse_sweep(cfg, Q, K, V, X, dense_ms, sub, 1, stream)
         progress("block sparsity done")
     out["gpu_clocks_during_layer_and_dense"] = keep["clocks"]
+    out["hbm_practical"] = hbm_practical(dev)
     if not args.no_cpu_baseline:
         Yc, idxc = keep["Y"], keep["idx"]
         out["cpu_baseline"], out["parity_vs_oracle"] = cpu_baseline(cfg, inp, keep["k"], keep["Lp"], Yc, idxc)

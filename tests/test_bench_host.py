@@ -95,3 +95,19 @@ def test_parity_verdict_accepts_the_oracle_and_rejects_planted_errors():
     assert not v["pass"] and v["heads_selection_equal"] == cfg.Hq - 1 and v["heads_within_tie_band"] == 0
     # a budget off by one is outside the coverage band
     assert not bench.parity_verdict(*args, k + 1, Lp, Y, idx)["budget_ok"]
+
+
+def test_stage_traffic_only_for_unchanged_sources(monkeypatch):
+    prof = CONFIGS[4]
+    got = bench.measured_stage_traffic(prof)
+    kv = dict(ln.split(":", 1) for ln in open(bench.STAGE_TRAFFIC_FILE) if ":" in ln and not ln.startswith("#"))
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    for st, src in bench.STAGE_SOURCES.items():
+        now = bench.source_hash(os.path.join(ROOT, "token_sparse_attention_amd", "csrc", src))
+        if kv[f"source_sha256_16 {src}"] == now:
+            assert got[st] == int(kv[f"{st}_hbm_bytes"])
+        else:
+            assert st not in got
+    assert bench.measured_stage_traffic(CONFIGS[5]) == {}
+    monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
+    assert bench.measured_stage_traffic(prof) == {}
