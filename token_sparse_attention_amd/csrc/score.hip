@@ -205,6 +205,17 @@ __device__ __forceinline__ double exp2_mc(float z, double c, double mc) {
   return (double)(__builtin_amdgcn_exp2f(hi) * fmaf(lo, 0.69314718055994531f, 1.0f));
 }
 
+// The fragments of one key row (`key`, zeros past L) as the matrix-core operand wants them: lane
+// half hf holds the 8 consecutive head-dim elements 16 ks + 8 hf of slice ks.
+template <int D>
+__device__ __forceinline__ void load_key_block(const uint16_t* __restrict__ K, int64_t L, int Hkv, int g,
+                                               int64_t key, int hf, bf16x8s_t (&kf)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    kf[ks] = key < L ? *reinterpret_cast<const bf16x8s_t*>(K + ((size_t)key * Hkv + g) * D + 16 * ks + 8 * hf)
+                     : bf16x8s_t{};
+}
+
 // LDS slot of 16-byte chunk c8 of staged query row r (XOR swizzle: 16 consecutive rows' reads of
 // one chunk land on distinct banks)
 template <int D>
@@ -246,20 +257,20 @@ __global__ __launch_bounds__(256) void score_p1_kernel(const uint16_t* __restric
     M[mb] = -INFINITY;
     S[mb] = 0.0;
   }
-  for (int sub = 0; sub < nsub; ++sub) {
+  // the wave's key blocks of 32, jb = 2 sub + kb; the next block's fragments load during this one's math
+  bf16x8s_t kn[KST];
+  load_key_block<D>(K, L, Hkv, g, (int64_t)blockIdx.x * bkeys + 64 * w + l32, hf, kn);
 #pragma unroll 1
-    for (int kb = 0; kb < 2; ++kb) {
-      // one block of 32 keys at a time (keeps registers low); z[r] below is key kbase + 8 (r / 4) +
-      // 4 hf + r % 4 of the lane's row
-      const int64_t kbase = (int64_t)blockIdx.x * bkeys + sub * kMSub + 64 * w + 32 * kb;
+  for (int jb = 0; jb < 2 * nsub; ++jb) {
+    {
+      // z[r] below is key kbase + 8 (r / 4) + 4 hf + r % 4 of the lane's row
+      const int64_t kbase = (int64_t)blockIdx.x * bkeys + (jb >> 1) * kMSub + 64 * w + 32 * (jb & 1);
       bf16x8s_t kf[KST];
-      {
-        const int64_t key = kbase + l32;
 #pragma unroll
-        for (int ks = 0; ks < KST; ++ks)
-          kf[ks] = key < L ? *reinterpret_cast<const bf16x8s_t*>(K + ((size_t)key * Hkv + g) * D + 16 * ks + 8 * hf)
-                           : bf16x8s_t{};
-      }
+      for (int ks = 0; ks < KST; ++ks) kf[ks] = kn[ks];
+      if (jb + 1 < 2 * nsub)
+        load_key_block<D>(K, L, Hkv, g, (int64_t)blockIdx.x * bkeys + ((jb + 1) >> 1) * kMSub + 64 * w + 32 * ((jb + 1) & 1) + l32,
+                          hf, kn);
 #pragma unroll
       for (int mb = 0; mb < kMRows / 32; ++mb) {
         if (mb >= MB) break;
@@ -353,16 +364,20 @@ __global__ __launch_bounds__(256, 2) void score_p2_kernel(const uint16_t* __rest
   // last-level cache still holds
   const int64_t kblk = (int64_t)gridDim.x - 1 - blockIdx.x;
   const bool open = (kblk + 1) * bkeys <= L - q + 1;
-  for (int sub = 0; sub < nsub; ++sub) {
+  // the wave's key blocks of 32, jb = 2 sub + kb; the next block's fragments load during this one's math
+  bf16x8s_t kn[KST];
+  load_key_block<D>(K, L, Hkv, g, kblk * bkeys + 64 * w + l32, hf, kn);
 #pragma unroll 1
-    for (int kb = 0; kb < 2; ++kb) {
-      // this lane's key and its fragments (one block of 32 keys at a time keeps registers low)
-      const int64_t key = kblk * bkeys + sub * kMSub + 64 * w + 32 * kb + l32;
+  for (int jb = 0; jb < 2 * nsub; ++jb) {
+    {
+      // this lane's key and its fragments
+      const int64_t key = kblk * bkeys + (jb >> 1) * kMSub + 64 * w + 32 * (jb & 1) + l32;
       bf16x8s_t kf[KST];
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks)
-        kf[ks] = key < L ? *reinterpret_cast<const bf16x8s_t*>(K + ((size_t)key * Hkv + g) * D + 16 * ks + 8 * hf)
-                         : bf16x8s_t{};
+      for (int ks = 0; ks < KST; ++ks) kf[ks] = kn[ks];
+      if (jb + 1 < 2 * nsub)
+        load_key_block<D>(K, L, Hkv, g, kblk * bkeys + ((jb + 1) >> 1) * kMSub + 64 * w + 32 * ((jb + 1) & 1) + l32,
+                          hf, kn);
       // visible to recent query i iff key - (L - q) <= i (always in workgroups before the window)
       const int64_t kr64 = key - (L - q);
       const int kr = open ? -1 : (int)(kr64 < -1 ? -1 : (kr64 > 1 << 20 ? 1 << 20 : kr64));
