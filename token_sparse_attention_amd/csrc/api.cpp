@@ -218,8 +218,9 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   int32_t* kLp = at<int32_t>(ws, g.kLp);
   int32_t* idx = at<int32_t>(ws, w.idx);
   int32_t* inv = at<int32_t>(ws, w.inv);
-  hipError_t e = fixed_ratio ? hipSuccess : launch_fill_zero(at<char>(ws, g.bhist), g.kLp - g.bhist, st);
-  if (e == hipSuccess) e = launch_fill_zero(at<char>(ws, g.shist), g.tcnt - g.shist, st);
+  // one clear covers the budget's and the selection's histograms and control words (and the two
+  // layer words between them, which the budget writes before anything reads them)
+  hipError_t e = launch_fill_zero(at<char>(ws, g.bhist), g.tcnt - g.bhist, st);
   if (e == hipSuccess)
     e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h, at<double2>(ws, g.partials),
                      at<double2>(ws, g.rowstat), st);
@@ -508,8 +509,7 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
     int32_t* idx = at<int32_t>(ws, w.idx) + Hq * (size_t)P[b];
     int32_t* inv = at<int32_t>(ws, w.inv) + Hq * (size_t)P[b];
     int32_t* kl = kLp + 2 * b;
-    e = launch_fill_zero(at<char>(ws, g.bhist), g.kLp - g.bhist, st);
-    if (e == hipSuccess) e = launch_fill_zero(at<char>(ws, g.shist), g.tcnt - g.shist, st);
+    e = launch_fill_zero(at<char>(ws, g.bhist), g.tcnt - g.bhist, st);   // histograms + control words
     if (e == hipSuccess)
       e = launch_score(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), Lb, s->Hq, s->Hkv, s->q, s_h,
                        at<double2>(ws, g.partials), at<double2>(ws, g.rowstat), st);
