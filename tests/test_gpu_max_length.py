@@ -1,0 +1,79 @@
+"""The longest supported sequence, L = 2^24, through the stage entry points (gather, compressed
+attention, scatter + residual) with two query heads, so per-head regions start past 4 GiB and the
+transposed value rows span the full capacity that the 32-bit buffer offsets of the attention allow.
+
+Each head keeps a seeded random selection of L' = 3000 tokens that includes the first and the last
+tokens of the sequence.  The attention therefore costs little, yet every address reaches the far
+end of its tensor.  Acceptance:
+- the gather is bit-exact against indexing the same stored tensors;
+- sampled attention rows are within 2e-2 + 1e-2 |ref| of the oracle, computed one by one;
+- Y at kept tokens equals X + O_hat (rounded once, as the scatter defines it) bit for bit, and at
+  dropped tokens it equals X bit for bit.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_sparse_attention_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+L, HQ, HKV, D, LP = 1 << 24, 2, 1, 128, 3000
+ATOL, RTOL = 2e-2, 1e-2
+
+
+@pytest.mark.timeout(300)
+def test_stages_at_the_maximum_length(gpu):
+    s = binding.shape(L, HQ, HKV, D, 16, 0.005, "bf16")
+    C = binding.capacity(L)
+    assert C == L
+    g = torch.Generator(device=gpu).manual_seed(24)
+    Q = torch.randn(L, HQ, D, device=gpu, generator=g).to(torch.bfloat16)
+    K = torch.randn(L, HKV, D, device=gpu, generator=g).to(torch.bfloat16)
+    V = torch.randn(L, HKV, D, device=gpu, generator=g).to(torch.bfloat16)
+    X = torch.randn(L, HQ, D, device=gpu, generator=g).to(torch.bfloat16)
+    rng = np.random.default_rng(24)
+    sel = []
+    for _ in range(HQ):
+        inner = rng.choice(np.arange(1, L - 4), LP - 5, replace=False)
+        sel.append(np.sort(np.concatenate([[0], inner, [L - 4, L - 3, L - 2, L - 1]])))
+    sel = np.stack(sel).astype(np.int64)
+    idx = torch.full((HQ, L), -1, dtype=torch.int32, device=gpu)
+    idx[:, :LP] = torch.from_numpy(sel.astype(np.int32)).to(gpu)
+    inv = torch.full((HQ, L), -1, dtype=torch.int32, device=gpu)
+    for h in range(HQ):
+        inv[h, torch.from_numpy(sel[h]).to(gpu)] = torch.arange(LP, dtype=torch.int32, device=gpu)
+    lp = torch.tensor([LP], dtype=torch.int32, device=gpu)
+
+    Qh = torch.empty(HQ, C, D, dtype=torch.bfloat16, device=gpu)
+    Kh, Oh = torch.empty_like(Qh), torch.empty_like(Qh)
+    Vht = torch.empty(HQ, D, C, dtype=torch.bfloat16, device=gpu)
+    binding.gather(s, Q, K, V, idx, lp, Qh, Kh, Vht)
+    binding.attn_causal(s, Qh, Kh, Vht, lp, Oh)
+    Y = torch.empty_like(X)
+    binding.scatter_residual(s, Oh, idx, inv, lp, X, Y)
+    torch.cuda.synchronize()
+
+    for h in range(HQ):
+        t = torch.from_numpy(sel[h]).to(gpu)
+        q_rows, k_rows, v_rows = Q[t, h].cpu(), K[t, 0].cpu(), V[t, 0].cpu()
+        assert torch.equal(Qh[h, :LP].cpu(), q_rows), h
+        assert torch.equal(Kh[h, :LP].cpu(), k_rows), h
+        assert torch.equal(Vht[h, :, :LP].cpu(), v_rows.T.contiguous()), h
+        rows = np.array([0, 1, 63, 64, 65, LP // 2, LP - 2, LP - 1])
+        want = oracle.attention_rows(q_rows.double().numpy(), k_rows.double().numpy(), v_rows.double().numpy(),
+                                     sel[h], rows)
+        rt = torch.from_numpy(rows).to(gpu)
+        got = Oh[h, rt].double().cpu().numpy()
+        err = np.abs(got - want)
+        assert (err <= ATOL + RTOL * np.abs(want)).all(), (h, float(err.max()))
+        # kept tokens: one fp32 sum of the stored values, rounded once to bf16
+        kept = torch.from_numpy(sel[h][rows]).to(gpu)
+        ref = (X[kept, h].float() + Oh[h, rt].float()).to(torch.bfloat16)
+        assert torch.equal(Y[kept, h], ref), h
+        # dropped tokens, including ones next to the last kept rows
+        dropped = np.setdiff1d(np.array([1, 2, L // 2, L - 6, L - 5]), sel[h])
+        dt = torch.from_numpy(dropped).to(gpu)
+        assert torch.equal(Y[dt, h], X[dt, h]), h
