@@ -77,3 +77,71 @@ def test_stages_at_the_maximum_length(gpu):
         dropped = np.setdiff1d(np.array([1, 2, L // 2, L - 6, L - 5]), sel[h])
         dt = torch.from_numpy(dropped).to(gpu)
         assert torch.equal(Y[dt, h], X[dt, h]), h
+
+
+@pytest.mark.timeout(300)
+def test_layer_at_the_maximum_length(gpu):
+    """The whole layer at L = 2^24 (tau = 0.9999 keeps ~1.7K tokens per head, so the attention is
+    small while score, budget and selection run over all 2^24 tokens).  Checked by properties that
+    hold at any size, on the GPU's own intermediate values:
+    - the fused layer equals the stage-by-stage sequence bit for bit, with the same keep count;
+    - every head's scores sum to q (each recent query's softmax sums to 1) and s_l sums to 1;
+    - k meets the coverage rule on the stored s_l (within 1e-6 relative of tau);
+    - each selection is exactly the top L' of s_h, ties to the lower index, in ascending order;
+    - sampled attention rows are within the bf16 tolerance of the oracle on the gathered rows."""
+    tau, q = 0.9999, 16
+    s = binding.shape(L, HQ, HKV, D, q, tau, "bf16")
+    C = binding.capacity(L)
+    g = torch.Generator(device=gpu).manual_seed(7)
+    Q = torch.randn(L, HQ, D, device=gpu, generator=g).to(torch.bfloat16)
+    K = torch.randn(L, HKV, D, device=gpu, generator=g).to(torch.bfloat16)
+    V = torch.randn(L, HKV, D, device=gpu, generator=g).to(torch.bfloat16)
+    X = torch.randn(L, HQ, D, device=gpu, generator=g).to(torch.bfloat16)
+
+    ws = binding.workspace(binding.layer_workspace_bytes(s), gpu)
+    kl_layer = torch.zeros(2, dtype=torch.int32, device=gpu)
+    Y = torch.empty_like(X)
+    binding.layer(s, Q, K, V, X, Y, kl_layer, ws)
+    del ws
+
+    sws = binding.workspace(binding.stage_workspace_bytes(s), gpu)
+    s_h = torch.empty(HQ, L, dtype=torch.float32, device=gpu)
+    s_l = torch.empty(L, dtype=torch.float32, device=gpu)
+    kl = torch.zeros(2, dtype=torch.int32, device=gpu)
+    idx = torch.empty(HQ, L, dtype=torch.int32, device=gpu)
+    inv = torch.empty_like(idx)
+    binding.score(s, Q, K, s_h, s_l, sws)
+    binding.budget(s, s_l, kl[0:1], kl[1:2], sws)
+    binding.select(s, s_h, kl[1:2], idx, inv, sws)
+    k, Lp = kl.tolist()
+    assert [k, Lp] == kl_layer.tolist()
+    assert 0 < Lp < 8192, Lp
+    Qh = torch.empty(HQ, C, D, dtype=torch.bfloat16, device=gpu)
+    Kh, Oh = torch.empty_like(Qh), torch.empty_like(Qh)
+    Vht = torch.empty(HQ, D, C, dtype=torch.bfloat16, device=gpu)
+    binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht)
+    binding.attn_causal(s, Qh, Kh, Vht, kl[1:2], Oh)
+    Y2 = torch.empty_like(X)
+    binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Y2)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+
+    sh = s_h.double().cpu().numpy()
+    sl = s_l.cpu().numpy()
+    for h in range(HQ):
+        assert abs(sh[h].sum() - q) <= 1e-5 * q, (h, sh[h].sum())
+    assert abs(sl.astype(np.float64).sum() - 1.0) <= 1e-5
+    cum = np.cumsum(np.sort(sl).astype(np.float64))
+    assert cum[k - 1] >= tau * (1 - 1e-6) and (k == 1 or cum[k - 2] < tau * (1 + 1e-6)), (k, cum[k - 2], cum[k - 1])
+    sel = idx[:, :Lp].cpu().numpy().astype(np.int64)
+    for h in range(HQ):
+        order = np.lexsort((np.arange(L), -s_h[h].cpu().numpy()))   # score desc, index asc
+        assert np.array_equal(sel[h], np.sort(order[:Lp])), h
+        t = torch.from_numpy(sel[h]).to(gpu)
+        q_rows, k_rows, v_rows = Q[t, h].cpu(), K[t, 0].cpu(), V[t, 0].cpu()
+        rows = np.array([0, 1, Lp // 2, Lp - 1])
+        want = oracle.attention_rows(q_rows.double().numpy(), k_rows.double().numpy(), v_rows.double().numpy(),
+                                     sel[h], rows)
+        got = Oh[h, torch.from_numpy(rows).to(gpu)].double().cpu().numpy()
+        err = np.abs(got - want)
+        assert (err <= ATOL + RTOL * np.abs(want)).all(), (h, float(err.max()))
