@@ -332,6 +332,31 @@ STAGE_SOURCES = {"score": "score.hip", "budget": "select.hip", "select": "select
 STAGE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stages_L131072_bf16.txt")
 
 
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_attention_L131072_bf16.txt")
+
+
+def measured_counters(cfg):
+    """The attention kernel's counted matrix-core busy fraction and instruction mix from the
+    committed counter summary, or None off the counted shape or once the kernel source changed."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("attention_source_sha256_16") != source_hash(ATTN_SOURCE):
+        return None
+    if (kv.get("workload_L"), kv.get("workload_Hq"), kv.get("workload_d")) != (str(cfg.L), str(cfg.Hq), str(cfg.d)):
+        return None
+    try:
+        return {"mfma_busy_fraction": float(kv["mfma_busy_fraction"]), "valu_per_mfma": float(kv["valu_per_mfma"]),
+                "lds_per_mfma": float(kv["lds_per_mfma"]), "lds_bank_conflicts": int(kv["lds_bank_conflicts"]),
+                "source": os.path.relpath(COUNTERS_FILE, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
 def traffic_probe(cfg, dev):
     """A short run for the counter passes: three compressed-attention launches on this workload's
     shape (L' = L, random bf16) and three copies of a 1 GiB buffer (the calibration of known size),
@@ -659,7 +684,8 @@ def main():
     out["roofline"] = {"bound": "mfma" if cfg.dtype == "bf16" else "alu",
                        "kernel": f"compressed causal attention ({cfg.dtype})",
                        "achieved": round(keep["att_tf"], 1), "peak": keep["peak"], "unit": "TFLOP/s",
-                       "frac": round(keep["att_tf"] / keep["peak"], 4), "traffic": measured_traffic(cfg)}
+                       "frac": round(keep["att_tf"] / keep["peak"], 4), "traffic": measured_traffic(cfg),
+                       "counters": measured_counters(cfg)}
     out["input_gen_s"] = round(t_gen, 1)
     sub = max(2, args.steps // 2)
     if not args.no_tau_sweep:

@@ -111,3 +111,17 @@ def test_stage_traffic_only_for_unchanged_sources(monkeypatch):
     assert bench.measured_stage_traffic(CONFIGS[5]) == {}
     monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
     assert bench.measured_stage_traffic(prof) == {}
+
+
+def test_attention_counters_only_on_the_counted_shape_and_source(monkeypatch):
+    got = bench.measured_counters(CONFIGS[4])
+    kv = dict(ln.split(":", 1) for ln in open(bench.COUNTERS_FILE) if ":" in ln and not ln.startswith("#"))
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv["attention_source_sha256_16"] == bench.source_hash(bench.ATTN_SOURCE):
+        assert got["mfma_busy_fraction"] == float(kv["mfma_busy_fraction"])
+        assert 0.0 < got["mfma_busy_fraction"] < 1.0 and got["lds_bank_conflicts"] >= 0
+    else:
+        assert got is None
+    assert bench.measured_counters(CONFIGS[5]) is None
+    monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
+    assert bench.measured_counters(CONFIGS[4]) is None
