@@ -617,6 +617,54 @@ def measure_workload(cfg, Q, K, V, X, steps, warmup, stream, sample_clocks=False
     return rec, {"Y": Y, "idx": idx, "k": k, "Lp": Lp, "clocks": clocks, "att_tf": att_tf, "peak": peak}
 
 
+def graph_replay(steps, warmup, stream, dev):
+    """The fused layer captured once in a HIP graph and replayed, against the same call made
+    eagerly, on the shorter workloads (where ~21 small launches weigh most) and on the varlen batch.
+    The library allocates nothing and never syncs, so one capture serves every replay; the replayed
+    output is checked bitwise against the eager one."""
+
+    def cap(fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    out = []
+    for n in (2, 3):
+        cfg = CONFIGS[n]
+        inp = make_layer(cfg)
+        Q, K, V, X = (inp[m].to(dev) for m in ("Q", "K", "V", "X"))
+        s = binding.shape_of(cfg)
+        ws = binding.workspace(binding.layer_workspace_bytes(s), dev)
+        Ye, Yg = torch.empty_like(X), torch.empty_like(X)
+        eager = timed(lambda: binding.layer(s, Q, K, V, X, Ye, None, ws), steps, warmup, stream)
+        g = cap(lambda: binding.layer(s, Q, K, V, X, Yg, None, ws))
+        replay = timed(g.replay, steps, warmup, stream)
+        out.append({"workload": cfg.name, "eager_ms": round(eager, 4), "graph_replay_ms": round(replay, 4),
+                    "bitwise_equal": bool(torch.equal(Ye, Yg))})
+        del g, Q, K, V, X, ws, Ye, Yg
+    cfg = CONFIGS[3]
+    b = make_batch(cfg, VARLEN_LENGTHS)
+    cu = [int(v) for v in b["cu_seqlens"]]
+    Q, K, V, X = (b[m].to(dev) for m in ("Q", "K", "V", "X"))
+    s = binding.shape(cu[-1], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, cfg.tau, cfg.dtype)
+    ws = binding.workspace(binding.layer_varlen_workspace_bytes(s, cu), dev)
+    Ye, Yg = torch.empty_like(X), torch.empty_like(X)
+    eager = timed(lambda: binding.layer_varlen(s, cu, Q, K, V, X, Ye, None, ws), steps, warmup, stream)
+    g = cap(lambda: binding.layer_varlen(s, cu, Q, K, V, X, Yg, None, ws))
+    replay = timed(g.replay, steps, warmup, stream)
+    out.append({"workload": f"varlen batch of {len(cu) - 1} ({cfg.name} recipe)", "eager_ms": round(eager, 4),
+                "graph_replay_ms": round(replay, 4), "bitwise_equal": bool(torch.equal(Ye, Yg))})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -627,6 +675,7 @@ def main():
     ap.add_argument("--no-tau-sweep", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-block-sparse", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay line")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload records of the other workloads")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -706,6 +755,9 @@ def main():
     if not args.no_varlen:
         out["supplementary_varlen"] = varlen_batch(sub, 1, stream, dev)
         progress("varlen batch done")
+    if not args.no_graph:
+        out["supplementary_graph"] = graph_replay(sub, 1, stream, dev)
+        progress("graph replay done")
     if not args.no_configs:
         recs = []
         for n in sorted(CONFIGS):
