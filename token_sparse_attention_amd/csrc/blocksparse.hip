@@ -104,7 +104,6 @@ __global__ __launch_bounds__(256) void block_select_kernel(const double* __restr
   __shared__ double red[4];
   __shared__ uint32_t kept[kSortMax / 32];
   __shared__ uint32_t wbase[kSortMax / 32];
-  __shared__ double tot[256];
   __shared__ int cut;
   const int I = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t Lp = Lp_dev[0];
@@ -179,19 +178,19 @@ __global__ __launch_bounds__(256) void block_select_kernel(const double* __restr
     const int per = (n + 255) / 256, lo = tid * per, hi = lo + per < n ? lo + per : n;
     double part = 0.0;
     for (int i = lo; i < hi; ++i) part += av[i];
-    // exclusive scan of the 256 chunk totals in thread order
-    tot[tid] = part;
-    __syncthreads();
-    if (tid == 0) {
-      double run = 0.0;
-      for (int t = 0; t < 256; ++t) {
-        const double v = tot[t];
-        tot[t] = run;
-        run += v;
-      }
+    // exclusive scan of the 256 chunk totals in thread order: a shuffle scan within each wave,
+    // then the wave totals in wave order (a fixed tree, so the result is deterministic)
+    double incl = part;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double nb2 = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += nb2;
     }
+    __syncthreads();                          // red[] is free again
+    if (lane == 63) red[w] = incl;
     __syncthreads();
-    double cum = tot[tid];
+    double cum = incl - part;
+    for (int v = 0; v < w; ++v) cum += red[v];
     for (int i = lo; i < hi; ++i) {
       cum += av[i];
       if (cum >= gamma) {
@@ -209,14 +208,15 @@ __global__ __launch_bounds__(256) void block_select_kernel(const double* __restr
   }
   __syncthreads();
   // ascending list: exclusive popcount scan over the bitmap words
-  const int nw = (n + 31) / 32;
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int i = 0; i < nw; ++i) {
-      wbase[i] = run;
-      run += __popc(kept[i]);
-    }
-    count[(size_t)h * nbmax + I] = (int32_t)run;
+  const int nw = (n + 31) / 32;              // at most kSortMax / 32 = 128: two words per lane
+  if (w == 0) {
+    const uint32_t c0 = 2 * lane < nw ? (uint32_t)__popc(kept[2 * lane]) : 0u;
+    const uint32_t c1 = 2 * lane + 1 < nw ? (uint32_t)__popc(kept[2 * lane + 1]) : 0u;
+    const uint64_t incl = wave_incl_scan_u64((uint64_t)(c0 + c1));
+    const uint32_t base = (uint32_t)incl - c0 - c1;
+    if (2 * lane < nw) wbase[2 * lane] = base;
+    if (2 * lane + 1 < nw) wbase[2 * lane + 1] = base + c0;
+    if (lane == 63) count[(size_t)h * nbmax + I] = (int32_t)incl;
   }
   __syncthreads();
   uint16_t* out = list + ((size_t)h * nbmax + I) * nbmax;
