@@ -153,20 +153,20 @@ __global__ __launch_bounds__(256) void block_select_kernel(const double* __restr
     }
   }
   __syncthreads();
-  // bitonic sort of P2 (weight, block) pairs into "before" order
+  // bitonic sort of P2 (weight, block) pairs into "before" order; a stage of distance j = 2^s has
+  // P2 / 2 pairs, and pair q is (i, i + j) with i = q with a zero bit inserted at bit s, so no
+  // thread idles on the upper half of a pair
   for (int k = 2; k <= P2; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P2; i += 256) {
-        const int p = i ^ j;
-        if (p > i) {
-          const bool up = (i & k) == 0;        // this run is sorted in "before" order
-          const double a0 = av[i], a1 = av[p];
-          const int j0 = jv[i], j1 = jv[p];
-          const bool swap = up ? before(a1, j1, a0, j0) : before(a0, j0, a1, j1);
-          if (swap) {
-            av[i] = a1; av[p] = a0;
-            jv[i] = (uint16_t)j1; jv[p] = (uint16_t)j0;
-          }
+    for (int j = k >> 1, sj = __ffs(j) - 1; j > 0; j >>= 1, --sj) {
+      for (int q = tid; q < P2 / 2; q += 256) {
+        const int i = ((q >> sj) << (sj + 1)) | (q & (j - 1)), p = i + j;
+        const bool up = (i & k) == 0;          // this run is sorted in "before" order
+        const double a0 = av[i], a1 = av[p];
+        const int j0 = jv[i], j1 = jv[p];
+        const bool swap = up ? before(a1, j1, a0, j0) : before(a0, j0, a1, j1);
+        if (swap) {
+          av[i] = a1; av[p] = a0;
+          jv[i] = (uint16_t)j1; jv[p] = (uint16_t)j0;
         }
       }
       __syncthreads();
