@@ -31,6 +31,8 @@
  *     from `Lp_dev` (one int32), so no host synchronisation is needed anywhere on the path.
  *   - NaN or Inf inputs give undefined outputs.  Calls on distinct streams with distinct workspaces
  *     may run concurrently; Y may alias X; no other aliasing is allowed.
+ *   - No call allocates, memsets or synchronises, so a call can be captured in a HIP graph on its
+ *     stream and replayed (workspaces are cleared by kernels inside the captured work).
  */
 #ifndef TSA_H
 #define TSA_H
