@@ -271,6 +271,36 @@ def test_tau_zero_layer_is_dense_attention_plus_residual(seed):
                                    sdpa_causal(Q[:, h], K[:, h // 2], V[:, h // 2]), rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(2))
+def test_sparse_layer_matches_library_attention_on_the_full_tensors(seed):
+    """A layer that really drops tokens, checked without compressing anything: for each query head,
+    the library's attention over the full-length tensors under the boolean mask "key kept by this
+    head and not after the query", with the library's own grouped-query head mapping (query heads
+    share a K/V head in consecutive groups), gives Y - X at the kept tokens; dropped tokens keep X
+    exactly.  This pins the gather (rows and K/V head), the compressed attention and the scatter
+    together, at per-head selections that differ and leave gaps."""
+    L, Hq, Hkv, d, q = 96, 6, 2, 16, 8
+    r = np.random.default_rng(40 + seed)
+    Q, K, V, X = (r.standard_normal(s) for s in ((L, Hq, d), (L, Hkv, d), (L, Hkv, d), (L, Hq, d)))
+    K[r.choice(L, 12, replace=False)] *= 4.0          # uneven scores, so the heads keep different sets
+    out = oracle.layer(Q, K, V, X, 0.3, q)
+    Lp, idx = out["Lp"], out["idx"]
+    assert 0 < Lp < L - 10
+    assert len({tuple(idx[h]) for h in range(Hq)}) > 1
+    kept = np.zeros((Hq, L), dtype=bool)
+    for h in range(Hq):
+        kept[h, idx[h]] = True
+    mask = kept[:, None, :] & np.tril(np.ones((L, L), dtype=bool))[None]
+    mask |= np.eye(L, dtype=bool)[None]                # rows of dropped queries: any finite output
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(1, 0, 2)))[None]
+    want = torch.nn.functional.scaled_dot_product_attention(
+        t(Q), t(K), t(V), attn_mask=torch.from_numpy(mask)[None], enable_gqa=True)[0].numpy()
+    for h in range(Hq):
+        np.testing.assert_allclose(out["Y"][idx[h], h] - X[idx[h], h], want[h, idx[h]], rtol=1e-11, atol=1e-12)
+        drop = ~kept[h]
+        assert (out["Y"][drop, h] == X[drop, h]).all()
+
+
 def test_tau_near_one_drops_everything_but_coverage():
     L, d = 30, 8
     Q, K, V, X = rnd((L, 2, d), 1), rnd((L, 2, d), 2), rnd((L, 2, d), 3), rnd((L, 2, d), 4)
@@ -503,6 +533,30 @@ def _mut_attention_no_scale(Qh, Kh, Vh, pos, rows=None):
     return e / e.sum(1, keepdims=True) @ Vh
 
 
+def _mut_gather_kv_interleaved(Q, K, V, idx):
+    Hq, Hkv = Q.shape[1], K.shape[1]
+    Qh = np.stack([Q[idx[h], h] for h in range(Hq)])
+    Kh = np.stack([K[idx[h], h % Hkv] for h in range(Hq)])
+    Vh = np.stack([V[idx[h], h % Hkv] for h in range(Hq)])
+    return Qh, Kh, Vh
+
+
+def _mut_gather_kv_prefix(Q, K, V, idx):
+    Hq, Hkv, Lp = Q.shape[1], K.shape[1], idx.shape[1]
+    G = Hq // Hkv
+    Qh = np.stack([Q[idx[h], h] for h in range(Hq)])
+    Kh = np.stack([K[:Lp, h // G] for h in range(Hq)])
+    Vh = np.stack([V[idx[h], h // G] for h in range(Hq)])
+    return Qh, Kh, Vh
+
+
+def _mut_decompress_prefix(Oh, idx, L):
+    Hq, Lp, d = Oh.shape
+    O = np.zeros((L, Hq, d))
+    O[:Lp] = Oh.transpose(1, 0, 2)
+    return O
+
+
 def _mut_ratio_floor(L, sparsity):
     k = math.floor(Fraction(float(np.float32(sparsity))) * L)
     return k, L - k
@@ -529,6 +583,12 @@ def _mut_block_no_diagonal(qbar, kbar, gamma):
     ("budget", _mut_budget_strict, lambda: test_budget_exhaustive_exact(0)),
     ("select", _mut_select_high_index_ties, test_select_zero_keys_keeps_the_prefix),
     ("attention_rows", _mut_attention_no_scale, lambda: test_dense_attention_matches_library(0)),
+    ("gather", _mut_gather_kv_interleaved,
+     lambda: test_sparse_layer_matches_library_attention_on_the_full_tensors(0)),
+    ("gather", _mut_gather_kv_prefix,
+     lambda: test_sparse_layer_matches_library_attention_on_the_full_tensors(0)),
+    ("decompress", _mut_decompress_prefix,
+     lambda: test_sparse_layer_matches_library_attention_on_the_full_tensors(0)),
 ])
 def test_planted_mistake_is_caught(monkeypatch, name, mutant, pin):
     monkeypatch.setattr(oracle, name, mutant)
