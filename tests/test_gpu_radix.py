@@ -1,0 +1,92 @@
+"""Budget and selection on both sides of the one-workgroup limit (rows of at most 32768 scores are
+budgeted and selected by a single workgroup per row, longer rows by the multi-block radix select).
+
+Scores are synthetic float32 rows, uploaded as they are, in four shapes: a narrow range (every key
+shares its leading bits), exact ties on a coarse grid, a wide range with exact zeros, and one
+repeated value.  Checks are exact:
+- k equals the smallest count of smallest float32 values whose exact sum reaches tau (integer
+  arithmetic on the float32 values), k + L' = L;
+- the selection is the oracle's top-L' of the same float32 scores (score descending, index
+  ascending), in ascending order; idx past L' is left as it was; inv is its inverse (-1 elsewhere).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from token_sparse_attention_amd import binding
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = [1, 5, 1023, 1025, 4097, 20001, 32768, 32769, 65537, 100003]
+
+
+def scores(kind, Hq, L, seed):
+    r = np.random.default_rng(seed)
+    if kind == "narrow":
+        s = 1.0 + r.random((Hq, L)) * 1e-3
+    elif kind == "ties":
+        s = r.integers(0, 6, size=(Hq, L)) * 0.125
+    elif kind == "wide":
+        s = np.exp(r.normal(0.0, 8.0, size=(Hq, L)))
+        s[r.random((Hq, L)) < 0.05] = 0.0
+    else:
+        s = np.full((Hq, L), 0.375)
+    return s.astype(np.float32)
+
+
+def exact_budget(vals32, tau32):
+    """Every float32 (and tau) times 2^149 is an integer: the budget in exact arithmetic."""
+    v = np.sort(vals32.astype(np.float64))
+    target = int(np.float64(tau32) * 2.0 ** 149)
+    if target <= 0:
+        return 0
+    acc = 0
+    for j, x in enumerate(v):
+        acc += int(x * 2.0 ** 149)
+        if acc >= target:
+            return j + 1
+    return len(v)
+
+
+@pytest.mark.parametrize("L", LENGTHS)
+@pytest.mark.parametrize("kind", ["narrow", "ties", "wide", "equal"])
+def test_select_exact(gpu, L, kind):
+    Hq = 3                                # odd: rows of odd L start off 16-byte boundaries
+    s = scores(kind, Hq, L, seed=L % 997)
+    s_h = torch.from_numpy(s).to(gpu)
+    shape = binding.shape(L, Hq, 1, 128, 1, 0.01, "bf16")
+    ws = binding.workspace(binding.stage_workspace_bytes(shape), gpu)
+    for Lp in sorted({0, 1, L // 3, L // 2, L - 1, L} - {-1}):
+        if Lp < 0 or Lp > L:
+            continue
+        idx = torch.full((Hq, L), -7, dtype=torch.int32, device=gpu)
+        inv = torch.full((Hq, L), -7, dtype=torch.int32, device=gpu)
+        binding.select(shape, s_h, torch.tensor([Lp], dtype=torch.int32, device=gpu), idx, inv, ws)
+        got, gi = idx.cpu().numpy(), inv.cpu().numpy()
+        want = oracle.select(s.astype(np.float64), Lp)
+        assert (got[:, :Lp] == want).all(), (kind, L, Lp)
+        assert (got[:, Lp:] == -7).all(), (kind, L, Lp)
+        for h in range(Hq):
+            w = np.full(L, -1)
+            w[want[h]] = np.arange(Lp)
+            assert (gi[h] == w).all(), (kind, L, Lp, h)
+
+
+@pytest.mark.parametrize("L", LENGTHS)
+@pytest.mark.parametrize("kind", ["narrow", "ties", "wide", "equal"])
+def test_budget_exact(gpu, L, kind):
+    s = scores(kind, 1, L, seed=L % 991 + 1)[0].astype(np.float64)
+    tot = s.sum()
+    s_l = (s / tot if tot > 0 else s).astype(np.float32)
+    d_sl = torch.from_numpy(s_l).to(gpu)
+    for tau in (0.0, 0.005, 0.3, 0.72, 0.9999):
+        t32 = float(np.float32(tau))
+        shape = binding.shape(L, 1, 1, 128, 1, tau, "bf16")
+        ws = binding.workspace(binding.stage_workspace_bytes(shape), gpu)
+        kl = torch.full((2,), -5, dtype=torch.int32, device=gpu)
+        binding.budget(shape, d_sl, kl[0:1], kl[1:2], ws)
+        k, Lp = kl.tolist()
+        assert k + Lp == L
+        assert k == exact_budget(s_l, t32), (kind, L, tau, k)

@@ -219,8 +219,9 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   int32_t* idx = at<int32_t>(ws, w.idx);
   int32_t* inv = at<int32_t>(ws, w.inv);
   // one clear covers the budget's and the selection's histograms and control words (and the two
-  // layer words between them, which the budget writes before anything reads them)
-  hipError_t e = launch_fill_zero(at<char>(ws, g.bhist), g.tcnt - g.bhist, st);
+  // layer words between them, which the budget writes before anything reads them); the one-workgroup
+  // selects of short rows use neither
+  hipError_t e = radix_resident(s->L) ? hipSuccess : launch_fill_zero(at<char>(ws, g.bhist), g.tcnt - g.bhist, st);
   if (e == hipSuccess)
     e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h, at<double2>(ws, g.partials),
                      at<double2>(ws, g.rowstat), st);
@@ -229,10 +230,9 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
       e = launch_budget_ratio(sparsity, s->L, kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
   } else {
     if (e == hipSuccess)
-      e = launch_layer_score(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l, st);
-    if (e == hipSuccess)
-      e = launch_budget(s_l, s->L, budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl),
-                        kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
+      e = launch_layer_score_budget(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l,
+                                    budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl),
+                                    kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
   }
   if (e == hipSuccess)
     e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
@@ -339,7 +339,7 @@ int tsa_budget(const tsa_shape* s, const float* s_l, int32_t* k_dev, int32_t* Lp
   const StageWs w = stage_layout(s);
   TSA_TRY(check_ws(ws, ws_bytes, w.total));
   hipStream_t st = stream_of(stream);
-  hipError_t e = launch_fill_zero(at<char>(ws, w.bhist), w.kLp - w.bhist, st);
+  hipError_t e = radix_resident(s->L) ? hipSuccess : launch_fill_zero(at<char>(ws, w.bhist), w.kLp - w.bhist, st);
   if (e == hipSuccess)
     e = launch_budget(s_l, s->L, budget_target(s->tau), at<uint64_t>(ws, w.bhist), at<RadixCtl>(ws, w.bctl),
                       at<int32_t>(ws, w.kLp), k_dev, Lp_dev, st);
@@ -355,7 +355,7 @@ int tsa_select(const tsa_shape* s, const float* s_h, const int32_t* Lp_dev, int3
   const StageWs w = stage_layout(s);
   TSA_TRY(check_ws(ws, ws_bytes, w.total));
   hipStream_t st = stream_of(stream);
-  hipError_t e = launch_fill_zero(at<char>(ws, w.shist), w.tcnt - w.shist, st);
+  hipError_t e = radix_resident(s->L) ? hipSuccess : launch_fill_zero(at<char>(ws, w.shist), w.tcnt - w.shist, st);
   if (e == hipSuccess)
     e = launch_select(s_h, s->L, s->Hq, Lp_dev, at<uint64_t>(ws, w.shist), at<RadixCtl>(ws, w.sctl),
                       at<uint32_t>(ws, w.tcnt), at<uint32_t>(ws, w.toff), idx, inv, st);
@@ -509,14 +509,15 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
     int32_t* idx = at<int32_t>(ws, w.idx) + Hq * (size_t)P[b];
     int32_t* inv = at<int32_t>(ws, w.inv) + Hq * (size_t)P[b];
     int32_t* kl = kLp + 2 * b;
-    e = launch_fill_zero(at<char>(ws, g.bhist), g.tcnt - g.bhist, st);   // histograms + control words
+    // histograms + control words (not used by the one-workgroup selects of short samples)
+    if (!radix_resident(Lb)) e = launch_fill_zero(at<char>(ws, g.bhist), g.tcnt - g.bhist, st);
     if (e == hipSuccess)
       e = launch_score(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), Lb, s->Hq, s->Hkv, s->q, s_h,
                        at<double2>(ws, g.partials), at<double2>(ws, g.rowstat), st);
-    if (e == hipSuccess) e = launch_layer_score(s_h, Lb, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l, st);
     if (e == hipSuccess)
-      e = launch_budget(s_l, Lb, budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl), kl,
-                        kLp_dev ? kLp_dev + 2 * b : nullptr, kLp_dev ? kLp_dev + 2 * b + 1 : nullptr, st);
+      e = launch_layer_score_budget(s_h, Lb, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l,
+                                    budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl), kl,
+                                    kLp_dev ? kLp_dev + 2 * b : nullptr, kLp_dev ? kLp_dev + 2 * b + 1 : nullptr, st);
     if (e == hipSuccess)
       e = launch_select(s_h, Lb, s->Hq, kl + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
                         at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);

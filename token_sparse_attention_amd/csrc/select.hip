@@ -11,6 +11,8 @@
 // computes the same value; block 0 stores it), so a pass is one launch and no host sync is needed.
 // Selection then keeps every score above the threshold plus the lowest-index ties at it, and
 // compacts the indices in ascending order with wave ballots and a per-head scan over tiles.
+// Rows of at most 32768 keys take a one-workgroup variant of both (below): the same integer
+// counts and weights, one launch per stage.
 #include "kern_common.h"
 #include "tsa_internal.h"
 
@@ -54,14 +56,22 @@ __global__ __launch_bounds__(256) void layer_sum_kernel(const float* __restrict_
 
 // total = sum of the tile sums (fixed order: strided per-thread partials, then a fixed tree),
 // stored after them at tile_sum[ntiles].
+// The first 256 threads form the partials; every thread of the block must call this (it holds a
+// barrier) and every thread gets the total.
+__device__ double tile_total(const double* __restrict__ tile_sum, int64_t ntiles, double* red) {
+  double a = 0.0;
+  if (threadIdx.x < 256)
+    for (int64_t i = threadIdx.x; i < ntiles; i += 256) a += tile_sum[i];
+  a = wave_sum(a);
+  if (threadIdx.x < 256 && (threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
 __global__ __launch_bounds__(256) void layer_total_kernel(double* __restrict__ tile_sum, int64_t ntiles) {
   __shared__ double red[4];
-  double a = 0.0;
-  for (int64_t i = threadIdx.x; i < ntiles; i += 256) a += tile_sum[i];
-  a = wave_sum(a);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
-  __syncthreads();
-  if (threadIdx.x == 0) tile_sum[ntiles] = (red[0] + red[1]) + (red[2] + red[3]);
+  const double total = tile_total(tile_sum, ntiles, red);
+  if (threadIdx.x == 0) tile_sum[ntiles] = total;
 }
 
 __global__ __launch_bounds__(256) void layer_norm_kernel(const double* __restrict__ S,
@@ -227,14 +237,299 @@ __global__ void budget_final_kernel(const uint64_t* __restrict__ hist, RadixCtl*
   }
 }
 
+// ---- one-workgroup selects for rows of at most kResidentMax keys ---------------------------------
+// A single 1024-thread workgroup per row holds the row in registers, NK consecutive keys per thread,
+// and runs every digit pass itself: one launch where the multi-block select needs one per pass.
+// Its digits start below the bits that every key of the row shares (the common leading bits of the
+// smallest and the largest key), so a row of similar scores is spread over many bins from the first
+// pass on, and they are 11 bits wide: at most three passes.  Counts and weights are integers, so the
+// crossing key, the counts below it and the ties at it are the same as the multi-block select's.
+constexpr int64_t kResidentMax = 32768;   // measured: at 65536 the multi-block budget is faster
+constexpr int kResThreads = 1024, kResWaves = kResThreads / kWave;
+constexpr int kResBits = 11, kResBins = 1 << kResBits;
+
+bool radix_resident(int64_t L) { return L <= kResidentMax; }
+
+// Two histograms: while wave 0 searches one pass's histogram, the other waves clear the next one's.
+template <bool MASS>
+struct ResShared {
+  uint32_t hc[2][kResBins];                  // counts
+  uint64_t hw[2][MASS ? kResBins : 1];       // weights (budget)
+  uint32_t rmin[kResWaves], rmax[kResWaves], rcnt[kResWaves];
+  uint64_t rw[kResWaves];
+  RadixCtl ctl;
+};
+
+// Clears histogram `buf` using the threads from `first` on.
+template <bool MASS>
+__device__ __forceinline__ void res_clear(ResShared<MASS>& sh, int buf, int first) {
+  for (int b = (int)threadIdx.x - first; b >= 0 && b < kResBins; b += kResThreads - first) {
+    sh.hc[buf][b] = 0;
+    if (MASS) sh.hw[buf][b] = 0;
+  }
+}
+
+// Exclusive prefix sum over the block (1024 threads); `total` receives the block sum.
+__device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* red, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) red[w] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kResWaves; ++i) {
+    const uint32_t r = red[i];
+    before += i < w ? r : 0u;
+    tot += r;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
+// Run by wave 0 after a pass's histogram over nbins bins: the bin where the ascending cumulative
+// weight (counts for a rank) first reaches T, given what lies below the current prefix.  Each lane
+// sums a contiguous chunk of per bins; the first lane whose running total reaches T owns the bin,
+// which a second scan over that chunk's bins (one per lane) then finds.
+template <bool MASS>
+__device__ void res_find(ResShared<MASS>& sh, int buf, int nbins, int width, uint32_t prefix, uint64_t cb,
+                         uint64_t wb, uint64_t T) {
+  const int lane = threadIdx.x & 63;
+  const int per = nbins >= 64 ? nbins >> 6 : 1;          // 1 .. 32
+  const int b0 = lane * per, n = b0 < nbins ? per : 0;
+  uint64_t cs = 0, ws = 0;
+#pragma unroll
+  for (int j = 0; j < kResBins / 64; ++j) {
+    if (j < n) {
+      const int b = b0 + ((j + lane) & (per - 1));      // rotated start: the lanes read distinct banks
+      const uint32_t c = sh.hc[buf][b];
+      cs += c;
+      ws += MASS ? sh.hw[buf][b] : (uint64_t)c;
+    }
+  }
+  const uint64_t wincl = wave_incl_scan_u64(ws), cincl = wave_incl_scan_u64(cs);
+  const uint64_t mask = __ballot(wb + wincl >= T);
+  if (mask == 0) {
+    if (lane == 0) sh.ctl.none = 1;
+    return;
+  }
+  const int f = __ffsll((long long)mask) - 1;
+  const uint64_t wbase = wb + __shfl(wincl - ws, f, kWave), cbase = cb + __shfl(cincl - cs, f, kWave);
+  const int bf = f * per;
+  uint32_t c2 = 0;
+  uint64_t w2 = 0;
+  if (lane < per) {
+    c2 = sh.hc[buf][bf + lane];
+    w2 = MASS ? sh.hw[buf][bf + lane] : (uint64_t)c2;
+  }
+  const uint64_t wi2 = wave_incl_scan_u64(w2), ci2 = wave_incl_scan_u64((uint64_t)c2);
+  // lane f's chunk reaches T, so some lane below per hits
+  const uint64_t m2 = __ballot(lane < per && wbase + wi2 >= T);
+  if (lane == __ffsll((long long)m2) - 1) {
+    sh.ctl.prefix = (prefix << width) | (uint32_t)(bf + lane);
+    sh.ctl.none = 0;
+    sh.ctl.cnt_below = cbase + ci2 - c2;
+    sh.ctl.w_below = wbase + wi2 - w2;
+    sh.ctl.n_bin = c2;
+  }
+}
+
+// The key where the ascending cumulative weight of the row first reaches T (T >= 1), with the
+// count and weight of the keys below it and the number of keys equal to it.  Thread j holds keys
+// NK j .. NK j + NK - 1 (those at or past L are absent).  Every thread returns the same result.
+struct ResResult {
+  uint32_t key, none;
+  uint64_t cnt_below, w_below, n_eq;
+};
+
+template <int NK, bool MASS>
+__device__ ResResult resident_threshold(const uint32_t (&key)[NK], int64_t L, uint64_t T, ResShared<MASS>& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t t0 = (int64_t)NK * tid;
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0;
+  uint64_t wt = 0;
+#pragma unroll
+  for (int i = 0; i < NK; ++i)
+    if (t0 + i < L) {
+      kmin = min(kmin, key[i]);
+      kmax = max(kmax, key[i]);
+      if (MASS) wt += weight_of<true>(key[i]);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o, kWave));
+    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, o, kWave));
+  }
+  if (MASS) wt = wave_sum_u64(wt);
+  if (lane == 0) {
+    sh.rmin[w] = kmin;
+    sh.rmax[w] = kmax;
+    sh.rw[w] = wt;
+  }
+  res_clear<MASS>(sh, 0, 0);
+  __syncthreads();
+  uint64_t wtot = 0;
+#pragma unroll
+  for (int i = 0; i < kResWaves; ++i) {
+    kmin = min(kmin, sh.rmin[i]);
+    kmax = max(kmax, sh.rmax[i]);
+    wtot += sh.rw[i];
+  }
+  ResResult r = {0u, 0u, 0, 0, 0};
+  if (T > (MASS ? wtot : (uint64_t)L)) {
+    r.none = 1;
+    return r;
+  }
+  const uint32_t diff = kmin ^ kmax;
+  int done = diff ? __clz((int)diff) : 32;                    // leading bits shared by every key
+  uint32_t prefix = done == 0 ? 0u : kmin >> (32 - done);
+  uint64_t cb = 0, wb = 0, n_eq = (uint64_t)L;
+  int buf = 0;                         // histogram of this pass (cleared)
+  while (done < 32) {
+    const int width = 32 - done < kResBits ? 32 - done : kResBits;
+    const int shift = 32 - done - width, nbins = 1 << width;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      uint32_t k = key[i];
+      // the weights are recomputed in each pass: hoisted out of the pass loop, 64-bit weights of
+      // every key would double the registers and spill
+      if (MASS) asm volatile("" : "+v"(k));
+      if (t0 + i < L && (done == 0 || (k >> (32 - done)) == prefix)) {
+        const uint32_t d = (k >> shift) & (uint32_t)(nbins - 1);
+        atomicAdd(&sh.hc[buf][d], 1u);
+        if (MASS) atomicAdd((unsigned long long*)&sh.hw[buf][d], (unsigned long long)weight_of<true>(k));
+      }
+    }
+    __syncthreads();
+    if (w == 0) res_find<MASS>(sh, buf, nbins, width, prefix, cb, wb, T);
+    else res_clear<MASS>(sh, buf ^ 1, kWave);
+    __syncthreads();
+    buf ^= 1;
+    if (sh.ctl.none) {                 // not reached: T is within the row's total
+      r.none = 1;
+      return r;
+    }
+    prefix = sh.ctl.prefix;
+    cb = sh.ctl.cnt_below;
+    wb = sh.ctl.w_below;
+    n_eq = sh.ctl.n_bin;
+    done += width;
+  }
+  r.key = prefix;
+  r.cnt_below = cb;
+  r.w_below = wb;
+  r.n_eq = n_eq;
+  return r;
+}
+
+// Thread j's NK consecutive values of a row of L floats (absent past L as 0).
+template <int NK>
+__device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t L, uint32_t (&key)[NK]) {
+  const int64_t t0 = (int64_t)NK * threadIdx.x;
+  if (t0 + NK <= L && ((reinterpret_cast<uintptr_t>(row + t0) & 15) == 0)) {
+#pragma unroll
+    for (int i = 0; i < NK; i += 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + t0 + i);
+      key[i] = v.x; key[i + 1] = v.y; key[i + 2] = v.z; key[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) key[i] = t0 + i < L ? __float_as_uint(row[t0 + i]) : 0u;
+  }
+}
+
+// Budget over one row.  FROM_S: s_l is first formed from the head sums S and their tile sums exactly
+// as launch_layer_score forms it (same total, same division) and stored.
+template <int NK, bool FROM_S>
+__global__ __launch_bounds__(kResThreads) void budget_resident_kernel(const float* __restrict__ s_l_in,
+                                                                      const double* __restrict__ S,
+                                                                      const double* __restrict__ tile_sum,
+                                                                      int64_t ntiles, float* __restrict__ s_l_out,
+                                                                      int64_t L, uint64_t T,
+                                                                      int32_t* __restrict__ kLp_ws,
+                                                                      int32_t* __restrict__ k_out,
+                                                                      int32_t* __restrict__ Lp_out) {
+  __shared__ ResShared<true> sh;
+  __shared__ double red[4];
+  uint32_t key[NK];
+  const int64_t t0 = (int64_t)NK * threadIdx.x;
+  if constexpr (FROM_S) {
+    const double total = tile_total(tile_sum, ntiles, red);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      key[i] = 0u;
+      if (t0 + i < L) {
+        const float v = (float)(S[t0 + i] / total);
+        s_l_out[t0 + i] = v;
+        key[i] = __float_as_uint(v);
+      }
+    }
+  } else {
+    load_keys<NK>(s_l_in, L, key);
+  }
+  int64_t k = 0;
+  if (T != 0) {
+    const ResResult r = resident_threshold<NK, true>(key, L, T, sh);
+    if (r.none) {
+      k = L;
+    } else {
+      const uint64_t V = weight_of<true>(r.key);
+      k = (int64_t)r.cnt_below + (int64_t)((T - r.w_below + V - 1) / V);
+    }
+  }
+  if (threadIdx.x == 0) {
+    if (kLp_ws) { kLp_ws[0] = (int32_t)k; kLp_ws[1] = (int32_t)(L - k); }
+    if (k_out) k_out[0] = (int32_t)k;
+    if (Lp_out) Lp_out[0] = (int32_t)(L - k);
+  }
+}
+
+template <bool FROM_S>
+static hipError_t launch_budget_resident(const float* s_l_in, const double* S, const double* tile_sum,
+                                         int64_t ntiles, float* s_l_out, int64_t L, uint64_t T, int32_t* kLp_ws,
+                                         int32_t* k_out, int32_t* Lp_out, hipStream_t st) {
+#define TSA_BUDGET_RES(NK) \
+  budget_resident_kernel<NK, FROM_S><<<1, kResThreads, 0, st>>>(s_l_in, S, tile_sum, ntiles, s_l_out, L, T, kLp_ws, k_out, Lp_out)
+  if (L <= 4 * kResThreads) TSA_BUDGET_RES(4);
+  else if (L <= 8 * kResThreads) TSA_BUDGET_RES(8);
+  else if (L <= 16 * kResThreads) TSA_BUDGET_RES(16);
+  else TSA_BUDGET_RES(32);
+#undef TSA_BUDGET_RES
+  return hipGetLastError();
+}
+
 hipError_t launch_budget(const float* s_l, int64_t L, uint64_t target, uint64_t* hist,
                          RadixCtl* ctl, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
                          hipStream_t st) {
+  if (radix_resident(L))
+    return launch_budget_resident<false>(s_l, nullptr, nullptr, 0, nullptr, L, target, kLp_ws, k_out, Lp_out, st);
   const dim3 grid((unsigned)((L + kHistTile - 1) / kHistTile), 1);
   for (int pass = 0; pass < kRadixPasses; ++pass)
     radix_hist_kernel<true><<<grid, 256, 0, st>>>(s_l, L, 0, pass, target, nullptr, hist, ctl);
   budget_final_kernel<<<1, 64, 0, st>>>(hist, ctl, L, target, kLp_ws, k_out, Lp_out);
   return hipGetLastError();
+}
+
+// Layer score and budget together.  For a row of at most kResidentMax tokens the budget's
+// workgroup also forms s_l (from the head sums and their tile sums, as launch_layer_score does), so
+// the layer score's total and normalisation launches are saved.
+hipError_t launch_layer_score_budget(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum, float* s_l,
+                                     uint64_t target, uint64_t* hist, RadixCtl* ctl, int32_t* kLp_ws,
+                                     int32_t* k_out, int32_t* Lp_out, hipStream_t st) {
+  if (!radix_resident(L)) {
+    hipError_t e = launch_layer_score(s_h, L, Hq, S, tile_sum, s_l, st);
+    return e == hipSuccess ? launch_budget(s_l, L, target, hist, ctl, kLp_ws, k_out, Lp_out, st) : e;
+  }
+  const unsigned n = (unsigned)(layer_tiles(L) - 1);
+  layer_sum_kernel<<<n, 256, 0, st>>>(s_h, L, Hq, S, tile_sum);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_budget_resident<true>(nullptr, S, tile_sum, n, s_l, L, target, kLp_ws, k_out, Lp_out, st);
 }
 
 // Fixed-ratio budget: k = round(s * L), halves up, exact on the float32 value of s (s in [0, 1]).
@@ -386,9 +681,73 @@ __global__ __launch_bounds__(256) void select_write_kernel(const float* __restri
   }
 }
 
+// Selection over one head's row per workgroup: the threshold key V = the (k+1)-th smallest score
+// (k = L - L'), every key above it plus the lowest-index ties at it, compacted in ascending order.
+template <int NK>
+__global__ __launch_bounds__(kResThreads) void select_resident_kernel(const float* __restrict__ s_h, int64_t L,
+                                                                      const int32_t* __restrict__ Lp_dev,
+                                                                      int32_t* __restrict__ idx,
+                                                                      int32_t* __restrict__ inv) {
+  __shared__ ResShared<false> sh;
+  __shared__ uint64_t smask[kResThreads];
+  __shared__ uint32_t sbase[kResThreads];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int64_t t0 = (int64_t)NK * tid;
+  uint32_t key[NK];
+  load_keys<NK>(s_h + (size_t)h * L, L, key);
+  const int64_t Lp = Lp_dev[0];
+  uint32_t V = 0xFFFFFFFFu;             // L' = 0: no key is above it or equal to it
+  uint64_t take_eq = 0;
+  if (Lp > 0) {
+    const ResResult r = resident_threshold<NK, false>(key, L, (uint64_t)(L - Lp + 1), sh);
+    if (!r.none) {
+      V = r.key;
+      take_eq = (uint64_t)Lp - ((uint64_t)L - r.cnt_below - r.n_eq);
+    }
+  }
+  uint32_t ceq = 0, tot;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) ceq += (t0 + i < L && key[i] == V) ? 1u : 0u;
+  uint32_t er = block_excl_scan_u32(ceq, sh.rcnt, tot);    // ties at V before this thread's keys
+  uint64_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    if (t0 + i >= L) continue;
+    bool keep = key[i] > V;
+    if (key[i] == V) keep = er++ < take_eq;
+    if (keep) m |= 1ull << i;
+  }
+  const uint32_t base = block_excl_scan_u32((uint32_t)__popcll(m), sh.rcnt, tot);
+  smask[tid] = m;
+  sbase[tid] = base;
+  __syncthreads();
+  int32_t* irow = idx + (size_t)h * L;
+  int32_t* vrow = inv ? inv + (size_t)h * L : nullptr;
+  for (int64_t e = tid; e < L; e += kResThreads) {
+    const int owner = (int)(e / NK), bit = (int)(e % NK);
+    const uint64_t mo = smask[owner];
+    const bool sel = (mo >> bit) & 1ull;
+    const int32_t pos = (int32_t)(sbase[owner] + (uint32_t)__popcll(mo & ((1ull << bit) - 1ull)));
+    if (sel) irow[pos] = (int32_t)e;
+    if (vrow) vrow[e] = sel ? pos : -1;
+  }
+}
+
+static hipError_t launch_select_resident(const float* s_h, int64_t L, int Hq, const int32_t* Lp_dev, int32_t* idx,
+                                         int32_t* inv, hipStream_t st) {
+#define TSA_SELECT_RES(NK) select_resident_kernel<NK><<<(unsigned)Hq, kResThreads, 0, st>>>(s_h, L, Lp_dev, idx, inv)
+  if (L <= 4 * kResThreads) TSA_SELECT_RES(4);
+  else if (L <= 8 * kResThreads) TSA_SELECT_RES(8);
+  else if (L <= 16 * kResThreads) TSA_SELECT_RES(16);
+  else TSA_SELECT_RES(32);
+#undef TSA_SELECT_RES
+  return hipGetLastError();
+}
+
 hipError_t launch_select(const float* s_h, int64_t L, int Hq, const int32_t* Lp_dev,
                          uint64_t* hist, RadixCtl* ctl, uint32_t* tile_cnt, uint32_t* tile_off,
                          int32_t* idx, int32_t* inv, hipStream_t st) {
+  if (radix_resident(L)) return launch_select_resident(s_h, L, Hq, Lp_dev, idx, inv, st);
   const dim3 hgrid((unsigned)((L + kHistTile - 1) / kHistTile), (unsigned)Hq);
   for (int pass = 0; pass < kRadixPasses; ++pass)
     radix_hist_kernel<false><<<hgrid, 256, 0, st>>>(s_h, L, L, pass, 0, Lp_dev, hist, ctl);

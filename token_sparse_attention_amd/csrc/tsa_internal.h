@@ -36,6 +36,13 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_budget(const float* s_l, int64_t L, uint64_t target, uint64_t* hist,
                          RadixCtl* ctl, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
                          hipStream_t st);
+// launch_layer_score followed by launch_budget (same s_l, k and L'), in fewer launches for short rows.
+hipError_t launch_layer_score_budget(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum, float* s_l,
+                                     uint64_t target, uint64_t* hist, RadixCtl* ctl, int32_t* kLp_ws,
+                                     int32_t* k_out, int32_t* Lp_out, hipStream_t st);
+// Rows of at most this many keys are budgeted and selected by one workgroup per row, which needs
+// neither the histograms nor the control words (nor their clearing).
+bool radix_resident(int64_t L);
 // Fixed-ratio budget: k = round(sparsity * L) (halves up); writes like launch_budget (kLp_ws may be null).
 hipError_t launch_budget_ratio(float sparsity, int64_t L, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out,
                                hipStream_t st);
