@@ -189,6 +189,20 @@ def algorithmic(cfg, Lp, union_rows):
 PARITY_TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}   # |gpu - ref| <= atol + rtol |ref|
 
 
+def host_info():
+    """The host the CPU baseline ran on: CPU model, logical CPUs and memory, from /proc."""
+    info = {"logical_cpus": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+        with open("/proc/meminfo") as f:
+            kib = next((int(ln.split()[1]) for ln in f if ln.startswith("MemTotal:")), None)
+        info["ram_gib"] = round(kib / 2 ** 20, 1) if kib else None
+    except OSError:
+        pass
+    return info
+
+
 def cpu_baseline(cfg, inp, k_gpu, Lp_gpu, Y_gpu, idx_gpu, budget_s=12.0):
     """The CPU oracle (float64, as it stands) on a bounded sample of the same workload, scaled to
     one full layer: scoring, budget and selection run in full; gather + attention run on a sample of
@@ -243,7 +257,7 @@ def cpu_baseline(cfg, inp, k_gpu, Lp_gpu, Y_gpu, idx_gpu, budget_s=12.0):
                        f"({t_sel:.1f} s); gather+attention on {n_rows} random rows of {len(heads)} heads "
                        f"({t_att:.1f} s) scaled by causal pair count to {cfg.Hq} heads x L'={Lp}; "
                        f"decompress+residual on {n_dec} rows scaled to L={cfg.L}"),
-            "oracle_k": int(k), "oracle_Lp": int(Lp), "gpu_Lp": int(Lp_gpu)}
+            "oracle_k": int(k), "oracle_Lp": int(Lp), "gpu_Lp": int(Lp_gpu), "host": host_info()}
     par = parity_verdict(cfg, inp["X"], s_h, s_l, k, Lp, idx, kept, k_gpu, Lp_gpu, Y_gpu, idx_gpu)
     return base, par
 
