@@ -27,9 +27,10 @@ def _compile(src, obj, extra):
     return r.stderr
 
 
-def build(extra=(), verbose=False):
-    """Compile every HIP/C++ source of the library and link libtsa.so.  Returns the library path."""
-    out = os.path.join(ROOT, "_build")
+def build(extra=(), verbose=False, lib_path=LIB, obj_dir=None):
+    """Compile every HIP/C++ source of the library and link libtsa.so (or lib_path, with the objects
+    in obj_dir, for a separately instrumented copy).  Returns the library path."""
+    out = obj_dir or os.path.join(ROOT, "_build")
     os.makedirs(out, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
     objs = [os.path.join(out, os.path.basename(s) + ".o") for s in srcs]
@@ -38,13 +39,13 @@ def build(extra=(), verbose=False):
     if verbose:
         for s, log in zip(srcs, logs):
             print(f"== {os.path.basename(s)}\n{log}")
-    tmp = LIB + ".tmp"
+    tmp = lib_path + ".tmp"
     r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
