@@ -209,28 +209,39 @@ __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ 
 }
 
 // The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
-// Grid (token tiles, heads); VPR consecutive lanes move one 16-byte chunk each of a row, so every
-// store instruction writes whole rows (whole cache lines, which the streaming hint needs: rows
-// written one 16-byte chunk per instruction lose the L2's merging, which cost 3.3 ms on a
-// 131072-token layer keeping a quarter of its tokens).  The inverse map is read once per
-// (token, head) group of lanes, and only unselected rows move.
+// A block takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
+// coalesced load into LDS, and a block whose tokens are all selected stops there.  Then VPR
+// consecutive lanes move one 16-byte chunk each of a row, so every store instruction writes whole
+// rows: whole cache lines, which the streaming hint needs.  Rows written one 16-byte chunk per
+// instruction lose the L2's merging, which cost 3.3 ms on a 131072-token layer keeping a quarter of
+// its tokens.  Measured at L = 131072 (32 heads): a layer keeping nearly every row took 75.6 us when
+// every lane read its row's inverse-map entry itself.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fill_unselected_kernel(const int32_t* __restrict__ inv, const T* __restrict__ X,
                                                               T* __restrict__ Y, int64_t L, int Hq) {
   constexpr int VPR = D * (int)sizeof(T) / 16;
-  constexpr int TPB = 256 / VPR;                  // tokens per block
+  constexpr int TPB = 256 / VPR;                  // rows per pass; VPR passes cover the 256 tokens
+  __shared__ int32_t sinv[256];
   const int h = blockIdx.y, c = threadIdx.x % VPR;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / VPR;
-  if (t >= L || inv[(size_t)h * L + t] >= 0) return;
-  const size_t e = ((size_t)t * Hq + h) * VPR + c;
+  const int64_t base = (int64_t)blockIdx.x * 256;
+  const int64_t tt = base + threadIdx.x;
+  const int32_t mine = tt < L ? inv[(size_t)h * L + tt] : 0;
+  sinv[threadIdx.x] = mine;
+  if (!__syncthreads_or(mine < 0)) return;        // every token of the block is selected
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
-  st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), reinterpret_cast<uint4*>(Y) + e);
+#pragma unroll
+  for (int p = 0; p < VPR; ++p) {
+    const int r = p * TPB + (int)threadIdx.x / VPR;
+    const int64_t t = base + r;
+    if (t >= L || sinv[r] >= 0) continue;
+    const size_t e = ((size_t)t * Hq + h) * VPR + c;
+    st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), reinterpret_cast<uint4*>(Y) + e);
+  }
 }
 
 template <typename T, int D>
 static hipError_t run_fill_unselected(const int32_t* inv, const void* X, void* Y, int64_t L, int Hq, hipStream_t st) {
-  constexpr int TPB = 256 / (D * (int)sizeof(T) / 16);
-  const dim3 grid((unsigned)((L + TPB - 1) / TPB), (unsigned)Hq);
+  const dim3 grid((unsigned)((L + 255) / 256), (unsigned)Hq);
   fill_unselected_kernel<T, D><<<grid, 256, 0, st>>>(inv, static_cast<const T*>(X), static_cast<T*>(Y), L, Hq);
   return hipGetLastError();
 }
