@@ -37,6 +37,13 @@ SMALL = {
                         salient_frac=0.0, shared_frac=1.0, seed=14),
     "tiny_L37": Workload("tiny_L37", L=37, Hq=8, Hkv=2, d=128, q=7, tau=0.1, dtype="bf16",
                          salient_frac=0.1, shared_frac=0.5, seed=15),
+    # q between 16 and 32: each head's recent rows padded to 32 in the matrix-core scoring
+    "gqa_q20": Workload("gqa_q20", L=900, Hq=8, Hkv=2, d=128, q=20, tau=0.03, dtype="bf16",
+                        salient_frac=0.03, shared_frac=0.5, seed=16),
+    # 16 heads sharing one KV head, q = 20: 512 padded rows per group, past the matrix-core scoring's
+    # 256, so bf16 takes the float64 vector-ALU scoring kernel
+    "big_group_bf16": Workload("big_group_bf16", L=600, Hq=16, Hkv=1, d=64, q=20, tau=0.02, dtype="bf16",
+                               salient_frac=0.03, shared_frac=1.0, seed=17),
 }
 
 
