@@ -269,6 +269,17 @@ __device__ __forceinline__ void res_clear(ResShared<MASS>& sh, int buf, int firs
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (32-bit: counts of at most kResidentMax keys).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = __shfl_up(v, o, kWave);
+    if (lane >= o) v += n;
+  }
+  return v;
+}
+
 // Exclusive prefix sum over the block (1024 threads); `total` receives the block sum.
 __device__ __forceinline__ uint32_t block_excl_scan_u32(uint32_t v, uint32_t* red, uint32_t& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -302,17 +313,20 @@ __device__ void res_find(ResShared<MASS>& sh, int buf, int nbins, int width, uin
   const int lane = threadIdx.x & 63;
   const int per = nbins >= 64 ? nbins >> 6 : 1;          // 1 .. 32
   const int b0 = lane * per, n = b0 < nbins ? per : 0;
-  uint64_t cs = 0, ws = 0;
+  // counts stay below 2^32 (at most kResidentMax keys); without masses the weight is the count
+  uint32_t cs = 0;
+  uint64_t ws = 0;
 #pragma unroll
   for (int j = 0; j < kResBins / 64; ++j) {
     if (j < n) {
       const int b = b0 + ((j + lane) & (per - 1));      // rotated start: the lanes read distinct banks
-      const uint32_t c = sh.hc[buf][b];
-      cs += c;
-      ws += MASS ? sh.hw[buf][b] : (uint64_t)c;
+      cs += sh.hc[buf][b];
+      if (MASS) ws += sh.hw[buf][b];
     }
   }
-  const uint64_t wincl = wave_incl_scan_u64(ws), cincl = wave_incl_scan_u64(cs);
+  const uint64_t cincl = wave_incl_scan_u32(cs);
+  if (!MASS) ws = cs;
+  const uint64_t wincl = MASS ? wave_incl_scan_u64(ws) : cincl;
   const uint64_t mask = __ballot(wb + wincl >= T);
   if (mask == 0) {
     if (lane == 0) sh.ctl.none = 1;
@@ -327,7 +341,8 @@ __device__ void res_find(ResShared<MASS>& sh, int buf, int nbins, int width, uin
     c2 = sh.hc[buf][bf + lane];
     w2 = MASS ? sh.hw[buf][bf + lane] : (uint64_t)c2;
   }
-  const uint64_t wi2 = wave_incl_scan_u64(w2), ci2 = wave_incl_scan_u64((uint64_t)c2);
+  const uint64_t ci2 = wave_incl_scan_u32(c2);
+  const uint64_t wi2 = MASS ? wave_incl_scan_u64(w2) : ci2;
   // lane f's chunk reaches T, so some lane below per hits
   const uint64_t m2 = __ballot(lane < per && wbase + wi2 >= T);
   if (lane == __ffsll((long long)m2) - 1) {
