@@ -21,7 +21,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from token_sparse_attention_amd import binding  # noqa: E402
-from token_sparse_attention_amd.configs import CONFIGS  # noqa: E402
+from token_sparse_attention_amd.configs import WORKLOADS  # noqa: E402
 from token_sparse_attention_amd.inputs import make_batch, make_layer  # noqa: E402
 
 METRIC = "TSA layer ms & speedup vs own dense attn at L=128K; MFMA util, HBM GB/s"
@@ -516,7 +516,7 @@ def varlen_batch(steps, warmup, stream, dev):
     """A ragged batch (8 samples of 4K-32K tokens, the 32K workload's recipe, one independent draw
     per sample): the batched layer with one attention launch over every sample's keep count, the
     same samples one tsa_layer call after another, and the batched dense baseline."""
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS[3]
     b = make_batch(cfg, VARLEN_LENGTHS)
     cu = [int(v) for v in b["cu_seqlens"]]
     Q, K, V, X = (b[n].to(dev) for n in ("Q", "K", "V", "X"))
@@ -652,7 +652,7 @@ def graph_replay(steps, warmup, stream, dev):
 
     out = []
     for n in (2, 3):
-        cfg = CONFIGS[n]
+        cfg = WORKLOADS[n]
         inp = make_layer(cfg)
         Q, K, V, X = (inp[m].to(dev) for m in ("Q", "K", "V", "X"))
         s = binding.shape_of(cfg)
@@ -664,7 +664,7 @@ def graph_replay(steps, warmup, stream, dev):
         out.append({"workload": cfg.name, "eager_ms": round(eager, 4), "graph_replay_ms": round(replay, 4),
                     "bitwise_equal": bool(torch.equal(Ye, Yg))})
         del g, Q, K, V, X, ws, Ye, Yg
-    cfg = CONFIGS[3]
+    cfg = WORKLOADS[3]
     b = make_batch(cfg, VARLEN_LENGTHS)
     cu = [int(v) for v in b["cu_seqlens"]]
     Q, K, V, X = (b[m].to(dev) for m in ("Q", "K", "V", "X"))
@@ -703,7 +703,7 @@ def main():
         print("bench.py needs an MI355X", file=sys.stderr)
         sys.exit(2)
 
-    cfg = CONFIGS[args.workload]
+    cfg = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     binding.lib()
     if args.traffic_probe:
@@ -774,10 +774,10 @@ def main():
         progress("graph replay done")
     if not args.no_configs:
         recs = []
-        for n in sorted(CONFIGS):
+        for n in sorted(WORKLOADS):
             if n == args.workload:
                 continue
-            c = CONFIGS[n]
+            c = WORKLOADS[n]
             t0 = time.perf_counter()
             part = make_layer(c)
             Qc, Kc, Vc, Xc = (part[m].to(dev) for m in ("Q", "K", "V", "X"))

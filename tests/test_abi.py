@@ -51,8 +51,8 @@ def test_check_args_length_limit():
 
 
 def test_check_args_accepts_the_workloads():
-    from token_sparse_attention_amd.configs import CONFIGS
-    for cfg in CONFIGS.values():
+    from token_sparse_attention_amd.configs import WORKLOADS
+    for cfg in WORKLOADS.values():
         assert binding.check_args(binding.shape_of(cfg)) == 0
     s = good()
     s.q = s.L = 7
@@ -134,10 +134,10 @@ def test_entry_points_validate_before_launch():
 
 
 def test_select_sparse_layers_rule():
-    from token_sparse_attention_amd.configs import CONFIGS
+    from token_sparse_attention_amd.configs import WORKLOADS
     from token_sparse_attention_amd.inputs import chain_drift_values
     from token_sparse_attention_amd.runtime import select_sparse_layers
-    cfg = CONFIGS[5]
+    cfg = WORKLOADS[5]
     assert select_sparse_layers(chain_drift_values(cfg)) == list(cfg.sparse_layers)
     assert select_sparse_layers([0.3, 0.1, 0.2, 0.1]) == [2, 4]
 

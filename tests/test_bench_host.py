@@ -11,7 +11,7 @@ import torch
 
 import bench
 import oracle
-from token_sparse_attention_amd.configs import CONFIGS
+from token_sparse_attention_amd.configs import WORKLOADS
 from token_sparse_attention_amd.inputs import make_layer
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -20,7 +20,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_traffic_only_for_the_profiled_shape():
     kv = dict(ln.split(":", 1) for ln in open(bench.TRAFFIC_FILE) if ":" in ln and not ln.startswith("#"))
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    prof = CONFIGS[4]
+    prof = WORKLOADS[4]
     assert (kv["workload_L"], kv["workload_Hq"], kv["workload_d"]) == (str(prof.L), str(prof.Hq), str(prof.d))
     t = bench.measured_traffic(prof)
     if kv["attention_source_sha256_16"] == bench.source_hash(bench.ATTN_SOURCE):
@@ -28,13 +28,13 @@ def test_traffic_only_for_the_profiled_shape():
     else:
         assert t is None
     # the 256K chain has another shape: its launch was never counted
-    assert bench.measured_traffic(CONFIGS[5]) is None
-    assert bench.measured_traffic(CONFIGS[2]) is None
+    assert bench.measured_traffic(WORKLOADS[5]) is None
+    assert bench.measured_traffic(WORKLOADS[2]) is None
 
 
 def test_traffic_null_when_source_changed(monkeypatch):
     monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
-    assert bench.measured_traffic(CONFIGS[4]) is None
+    assert bench.measured_traffic(WORKLOADS[4]) is None
 
 
 def test_multi_gpu_request_is_refused():
@@ -65,7 +65,7 @@ def _oracle_run(cfg):
 
 
 def test_parity_verdict_accepts_the_oracle_and_rejects_planted_errors():
-    cfg = CONFIGS[1]
+    cfg = WORKLOADS[1]
     inp, r, Y, idx, kept = _oracle_run(cfg)
     k, Lp = r["k"], r["Lp"]
     args = (cfg, inp["X"], r["s_h"], r["s_l"], k, Lp, r["idx"], kept)
@@ -98,7 +98,7 @@ def test_parity_verdict_accepts_the_oracle_and_rejects_planted_errors():
 
 
 def test_stage_traffic_only_for_unchanged_sources(monkeypatch):
-    prof = CONFIGS[4]
+    prof = WORKLOADS[4]
     got = bench.measured_stage_traffic(prof)
     kv = dict(ln.split(":", 1) for ln in open(bench.STAGE_TRAFFIC_FILE) if ":" in ln and not ln.startswith("#"))
     kv = {k.strip(): v.strip() for k, v in kv.items()}
@@ -108,13 +108,13 @@ def test_stage_traffic_only_for_unchanged_sources(monkeypatch):
             assert got[st] == int(kv[f"{st}_hbm_bytes"])
         else:
             assert st not in got
-    assert bench.measured_stage_traffic(CONFIGS[5]) == {}
+    assert bench.measured_stage_traffic(WORKLOADS[5]) == {}
     monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
     assert bench.measured_stage_traffic(prof) == {}
 
 
 def test_attention_counters_only_on_the_counted_shape_and_source(monkeypatch):
-    got = bench.measured_counters(CONFIGS[4])
+    got = bench.measured_counters(WORKLOADS[4])
     kv = dict(ln.split(":", 1) for ln in open(bench.COUNTERS_FILE) if ":" in ln and not ln.startswith("#"))
     kv = {k.strip(): v.strip() for k, v in kv.items()}
     if kv["attention_source_sha256_16"] == bench.source_hash(bench.ATTN_SOURCE):
@@ -122,6 +122,6 @@ def test_attention_counters_only_on_the_counted_shape_and_source(monkeypatch):
         assert 0.0 < got["mfma_busy_fraction"] < 1.0 and got["lds_bank_conflicts"] >= 0
     else:
         assert got is None
-    assert bench.measured_counters(CONFIGS[5]) is None
+    assert bench.measured_counters(WORKLOADS[5]) is None
     monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
-    assert bench.measured_counters(CONFIGS[4]) is None
+    assert bench.measured_counters(WORKLOADS[4]) is None

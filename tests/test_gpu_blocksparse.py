@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from token_sparse_attention_amd import binding
-from token_sparse_attention_amd.configs import CONFIGS, Workload, scaled
+from token_sparse_attention_amd.configs import WORKLOADS, Workload, scaled
 from token_sparse_attention_amd.inputs import make_layer
 
 pytestmark = pytest.mark.gpu
@@ -29,7 +29,7 @@ CASES = {
                               salient_frac=0.03, shared_frac=0.5, sink=8, seed=42),
     "f32_d128_L300": Workload("bs_f32", L=300, Hq=2, Hkv=2, d=128, q=3, tau=0.02, dtype="f32",
                               salient_frac=0.05, shared_frac=1.0, seed=43),
-    "bf16_L4096_h8": scaled(CONFIGS[2], 4096, Hq=8, Hkv=2, seed=44),
+    "bf16_L4096_h8": scaled(WORKLOADS[2], 4096, Hq=8, Hkv=2, seed=44),
 }
 
 

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 from token_sparse_attention_amd import binding
-from token_sparse_attention_amd.configs import CONFIGS, scaled
+from token_sparse_attention_amd.configs import WORKLOADS, scaled
 from token_sparse_attention_amd.inputs import chain_drift_values, iter_chain
 from token_sparse_attention_amd.runtime import select_sparse_layers
 
@@ -32,7 +32,7 @@ ATOL, RTOL = 2e-2, 1e-2
 
 @pytest.mark.timeout(600)
 def test_chain_end_to_end_against_float64(gpu):
-    cfg = scaled(CONFIGS[5], 2048, Hq=8, Hkv=2)
+    cfg = scaled(WORKLOADS[5], 2048, Hq=8, Hkv=2)
     sparse = select_sparse_layers(chain_drift_values(cfg))
     assert sparse == list(cfg.sparse_layers)
     s = binding.shape_of(cfg)

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from token_sparse_attention_amd import binding
-from token_sparse_attention_amd.configs import CONFIGS, Workload, scaled
+from token_sparse_attention_amd.configs import WORKLOADS, Workload, scaled
 from token_sparse_attention_amd.inputs import make_batch, make_layer
 
 pytestmark = pytest.mark.gpu
@@ -28,7 +28,7 @@ def capture(fn):
     return g
 
 
-@pytest.mark.parametrize("cfg", [scaled(CONFIGS[2], 2048, Hq=8, Hkv=2, seed=61),
+@pytest.mark.parametrize("cfg", [scaled(WORKLOADS[2], 2048, Hq=8, Hkv=2, seed=61),
                                  Workload("graph_f32", L=300, Hq=2, Hkv=2, d=128, q=3, tau=0.02, dtype="f32",
                                           salient_frac=0.05, shared_frac=1.0, seed=62)],
                          ids=["bf16_L2048", "f32_L300"])

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from token_sparse_attention_amd import binding
-from token_sparse_attention_amd.configs import CONFIGS
+from token_sparse_attention_amd.configs import WORKLOADS
 from token_sparse_attention_amd.inputs import chain_drift_values, iter_chain, make_layer
 from token_sparse_attention_amd.runtime import select_sparse_layers
 
@@ -106,7 +106,7 @@ def check_layer_output(cfg, inp, X_in, Y, idx, heads, seed):
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("num", [3, 4])
 def test_single_layer_full_size(gpu, num):
-    cfg = CONFIGS[num]
+    cfg = WORKLOADS[num]
     print(f"\n[{cfg.name}] generating inputs", flush=True)
     inp = make_layer(cfg)
     Q, K, V, X = (inp[n].to(gpu) for n in ("Q", "K", "V", "X"))
@@ -144,7 +144,7 @@ def test_chain_8_layers_256k(gpu):
     """Eight attention-only layers at L = 256K with the residual carried in place; the least
     drifting half (layers 5-8, chosen from the seeded drift values) run Token Sparse Attention.
     Each layer is checked on the GPU's stored input of that layer, so errors do not compound."""
-    cfg = CONFIGS[5]
+    cfg = WORKLOADS[5]
     sparse = select_sparse_layers(chain_drift_values(cfg))
     assert sparse == list(cfg.sparse_layers)
     s = binding.shape_of(cfg)

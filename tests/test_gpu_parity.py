@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from token_sparse_attention_amd import binding
-from token_sparse_attention_amd.configs import CONFIGS, Workload, scaled
+from token_sparse_attention_amd.configs import WORKLOADS, Workload, scaled
 from token_sparse_attention_amd.inputs import make_layer
 
 pytestmark = pytest.mark.gpu
@@ -25,8 +25,8 @@ pytestmark = pytest.mark.gpu
 TOL = {"bf16": (2e-2, 1e-2), "f32": (1e-4, 1e-4)}
 
 SMALL = {
-    "c1": CONFIGS[1],
-    "c2": CONFIGS[2],
+    "c1": WORKLOADS[1],
+    "c2": WORKLOADS[2],
     "gqa_ragged_q5": Workload("gqa_ragged_q5", L=1000, Hq=4, Hkv=2, d=128, q=5, tau=0.05, dtype="bf16",
                               salient_frac=0.02, shared_frac=0.5, seed=11),
     "d64_bf16_odd": Workload("d64_bf16_odd", L=777, Hq=2, Hkv=1, d=64, q=16, tau=0.01, dtype="bf16",
@@ -353,7 +353,7 @@ def test_dense_attention(case):
 
 
 def test_tau_zero_layer_equals_dense_plus_residual(gpu):
-    cfg = scaled(CONFIGS[2], 1536, Hq=4, Hkv=2, tau=0.0)
+    cfg = scaled(WORKLOADS[2], 1536, Hq=4, Hkv=2, tau=0.0)
     c = Case(cfg, gpu)
     ws = binding.workspace(binding.layer_workspace_bytes(c.s), gpu)
     kl = torch.zeros(2, dtype=torch.int32, device=gpu)

@@ -2,4 +2,4 @@
 and a thin ctypes binding.  Importing the package loads nothing; the library is opened on first use
 and a missing library is an error, never a fallback."""
 
-from .configs import CONFIGS, Workload  # noqa: F401
+from .configs import WORKLOADS, Workload  # noqa: F401

@@ -31,7 +31,7 @@ class Workload:
     sparse_layers: tuple = field(default_factory=tuple)  # 1-based ids of sparse layers (chain only)
 
 
-CONFIGS = {
+WORKLOADS = {
     1: Workload("tiny_fp32_L1024_H4_d64", L=1024, Hq=4, Hkv=4, d=64, q=16, tau=0.005, dtype="f32",
                 salient_frac=0.03, shared_frac=1.0, seed=1),
     2: Workload("bf16_L4096_H32_d128", L=4096, Hq=32, Hkv=32, d=128, q=16, tau=0.005, dtype="bf16",
