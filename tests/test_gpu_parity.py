@@ -40,6 +40,9 @@ SMALL = {
     # q between 16 and 32: each head's recent rows padded to 32 in the matrix-core scoring
     "gqa_q20": Workload("gqa_q20", L=900, Hq=8, Hkv=2, d=128, q=20, tau=0.03, dtype="bf16",
                         salient_frac=0.03, shared_frac=0.5, seed=16),
+    # 64 query / 8 KV heads (groups of 8, 128 recent rows each in the matrix-core scoring)
+    "gqa8_h64": Workload("gqa8_h64", L=300, Hq=64, Hkv=8, d=128, q=16, tau=0.02, dtype="bf16",
+                         salient_frac=0.03, shared_frac=0.5, seed=18),
     # 16 heads sharing one KV head, q = 20: 512 padded rows per group, past the matrix-core scoring's
     # 256, so bf16 takes the float64 vector-ALU scoring kernel
     "big_group_bf16": Workload("big_group_bf16", L=600, Hq=16, Hkv=1, d=64, q=20, tau=0.02, dtype="bf16",
