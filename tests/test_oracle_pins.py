@@ -96,6 +96,12 @@ def test_layer_score_normalised_and_equal_heads():
     np.testing.assert_allclose(s_l, s_h[0] / q, rtol=1e-12)
 
 
+def test_layer_score_hand_case():
+    """Heads that disagree: column sums (1, 2, 5) over a total of 8, a head's zero kept as zero."""
+    s_h = np.array([[1.0, 0.0, 3.0], [0.0, 2.0, 2.0]])
+    assert oracle.layer_score(s_h).tolist() == [0.125, 0.25, 0.625]
+
+
 # -- budget ---------------------------------------------------------------------------------------
 
 def brute_budget(vals, tau):
@@ -576,7 +582,46 @@ def _mut_block_no_diagonal(qbar, kbar, gamma):
     return keep
 
 
+def _mut_layer_score_unnormalised(s_h):
+    return s_h.sum(axis=0)
+
+
+def _mut_layer_score_max(s_h):
+    S = s_h.max(axis=0)
+    return S / S.sum()
+
+
+def _mut_residual_sign(X, O):
+    return X - O
+
+
+def _mut_pool_full_block(Xh, Lp, B=oracle.BLOCK):
+    nb = -(-Lp // B)
+    out = np.zeros((nb, Xh.shape[1]))
+    for b in range(nb):
+        out[b] = (Xh[b * B: min(Lp, (b + 1) * B)].sum(axis=0) / B).astype(np.float32)
+    return out
+
+
+def _mut_drift_squared(h_cur, h_next, eps=1e-6):
+    num = np.linalg.norm(h_next - h_cur, axis=1) ** 2
+    den = np.linalg.norm(h_cur, axis=1) ** 2 + eps
+    return float(np.mean(num / den))
+
+
+def _mut_sparse_most_drifting(R, delta=0.5):
+    N = len(R)
+    order = sorted(range(N), key=lambda i: (-R[i], i))
+    return sorted(i + 1 for i in order[: int(delta * N)])
+
+
 @pytest.mark.parametrize("name,mutant,pin", [
+    ("layer_score", _mut_layer_score_unnormalised, test_layer_score_normalised_and_equal_heads),
+    ("layer_score", _mut_layer_score_max, test_layer_score_hand_case),
+    ("residual", _mut_residual_sign, lambda: test_tau_zero_layer_is_dense_attention_plus_residual(0)),
+    ("block_pool", _mut_pool_full_block, test_block_pool_is_the_block_mean),
+    ("representation_drift", _mut_drift_squared, test_sparse_layers_and_drift),
+    ("sparse_layers", _mut_sparse_most_drifting, test_sparse_layers_and_drift),
     ("budget_fixed_ratio", _mut_ratio_floor, test_budget_fixed_ratio_hand_cases),
     ("block_select", _mut_block_no_diagonal, test_block_select_hand_case),
     ("head_scores", _mut_no_causal, lambda: test_score_zero_keys_closed_form(64, 16)),
