@@ -47,6 +47,9 @@ SMALL = {
     # 256, so bf16 takes the float64 vector-ALU scoring kernel
     "big_group_bf16": Workload("big_group_bf16", L=600, Hq=16, Hkv=1, d=64, q=20, tau=0.02, dtype="bf16",
                                salient_frac=0.03, shared_frac=1.0, seed=17),
+    # fp32 with grouped heads, d = 64, a sink and a length that leaves a ragged last tile
+    "f32_d64_gqa": Workload("f32_d64_gqa", L=517, Hq=6, Hkv=2, d=64, q=9, tau=0.05, dtype="f32",
+                            salient_frac=0.03, shared_frac=0.5, sink=4, seed=19),
 }
 
 
