@@ -553,6 +553,24 @@ def varlen_batch(steps, warmup, stream, dev):
     return out
 
 
+def varlen_trace(dev, calls=5):
+    """A short run for a kernel trace of the batched layer: the varlen batch above at the 32K
+    workload's tau, one warm-up call, then `calls` calls of tsa_layer_varlen."""
+    cfg = WORKLOADS[3]
+    b = make_batch(cfg, VARLEN_LENGTHS)
+    cu = [int(v) for v in b["cu_seqlens"]]
+    Q, K, V, X = (b[n].to(dev) for n in ("Q", "K", "V", "X"))
+    del b
+    s = binding.shape(cu[-1], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, cfg.tau, cfg.dtype)
+    ws = binding.workspace(binding.layer_varlen_workspace_bytes(s, cu), dev)
+    kLp = torch.zeros(len(cu) - 1, 2, dtype=torch.int32, device=dev)
+    Y = torch.empty_like(X)
+    for _ in range(calls + 1):
+        binding.layer_varlen(s, cu, Q, K, V, X, Y, kLp, ws)
+    torch.cuda.synchronize()
+    progress(f"varlen trace: {calls + 1} calls of tsa_layer_varlen, keep counts {kLp[:, 1].tolist()}")
+
+
 def measure_workload(cfg, Q, K, V, X, steps, warmup, stream, sample_clocks=False):
     """Everything timed on one workload with inputs resident in HBM: the whole layer and the dense
     baseline alternately step by step, then every stage through its own ABI call (memory-bound
@@ -694,6 +712,8 @@ def main():
                     help="skip the per-workload records of the other workloads")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the short kernel sequence used for the rocprofv3 counter passes")
+    ap.add_argument("--varlen-trace", action="store_true",
+                    help="only run the varlen batch's layer a few times, for a rocprofv3 kernel trace")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the layer runs on one MI355X (no multi-GPU path is built); "
@@ -708,6 +728,9 @@ def main():
     binding.lib()
     if args.traffic_probe:
         traffic_probe(cfg, dev)
+        return
+    if args.varlen_trace:
+        varlen_trace(dev)
         return
     t_gen = time.perf_counter()
     inp = make_layer(cfg)
