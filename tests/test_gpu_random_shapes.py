@@ -9,6 +9,7 @@ from 1 to ~2500 (log-uniform, so most lengths leave a ragged last tile), the rec
 - the fused layer's keep counts equal the stage calls'; rows outside a head's selection equal X
   bit for bit; every selected row within 2e-2 + 1e-2 |ref| (bf16) or 1e-4 + 1e-4 |ref| (fp32) of
   the oracle's attention on the GPU's selection plus X.
+Every third draw also runs the fixed-ratio layer at a random sparsity.
 """
 
 import numpy as np
@@ -121,3 +122,46 @@ def test_random_shape_layer(gpu, seed):
         bad = np.abs(got[pos, hh] - want) > atol + rtol * np.abs(want)
         assert not bad.any(), (hh, int(bad.sum()), float(np.abs(got[pos, hh] - want).max()))
     print(f"[{cfg.name}] k={k} L'={Lp} ok", flush=True)
+
+
+@pytest.mark.timeout(120)
+@pytest.mark.parametrize("seed", range(0, 96, 3))
+def test_random_shape_layer_fixed_ratio(gpu, seed):
+    """The fixed-ratio layer on every third draw, at a random sparsity in [0, 1): k exactly the
+    oracle's integer rule, the selection exactly the oracle's on the GPU's scores, unselected rows
+    equal to X bit for bit, selected rows within the tolerance of the oracle's attention plus X."""
+    cfg = draw(seed)
+    sparsity = float(np.random.default_rng(7000 + seed).uniform(0.0, 1.0))
+    print(f"\n[{cfg.name}] {cfg} sparsity={sparsity:.4f}", flush=True)
+    L, Hq, Hkv = cfg.L, cfg.Hq, cfg.Hkv
+    inp = make_layer(cfg)
+    Q, K, V, X = (inp[n].to(gpu) for n in ("Q", "K", "V", "X"))
+    h = {n: f64(inp[n]) for n in ("Q", "K", "V", "X")}
+    s = binding.shape_of(cfg)
+    lws = binding.workspace(binding.layer_workspace_bytes(s), gpu)
+    kl = torch.zeros(2, dtype=torch.int32, device=gpu)
+    Y = torch.empty_like(X)
+    binding.layer_ratio(s, sparsity, Q, K, V, X, Y, kl, lws)
+    k, Lp = kl.tolist()
+    assert (k, Lp) == oracle.budget_fixed_ratio(L, sparsity)
+    sws = binding.workspace(binding.stage_workspace_bytes(s), gpu)
+    s_h = torch.empty(Hq, L, dtype=torch.float32, device=gpu)
+    s_l = torch.empty(L, dtype=torch.float32, device=gpu)
+    binding.score(s, Q, K, s_h, s_l, sws)
+    idx_t = torch.empty(Hq, L, dtype=torch.int32, device=gpu)
+    binding.select(s, s_h, kl[1:2], idx_t, None, sws)
+    idx = idx_t[:, :Lp].cpu().numpy().astype(np.int64)
+    assert (idx == oracle.select(f64(s_h), Lp)).all()
+    got = f64(Y)
+    G = Hq // Hkv
+    atol, rtol = TOL[cfg.dtype]
+    for hh in range(Hq):
+        un = np.setdiff1d(np.arange(L), idx[hh])
+        assert (got[un, hh] == h["X"][un, hh]).all(), hh
+        if Lp == 0:
+            continue
+        pos = idx[hh]
+        O = oracle.attention_rows(h["Q"][pos, hh], h["K"][pos, hh // G], h["V"][pos, hh // G], pos)
+        want = h["X"][pos, hh] + O
+        bad = np.abs(got[pos, hh] - want) > atol + rtol * np.abs(want)
+        assert not bad.any(), (hh, int(bad.sum()), float(np.abs(got[pos, hh] - want).max()))
