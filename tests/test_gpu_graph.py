@@ -29,9 +29,12 @@ def capture(fn):
 
 
 @pytest.mark.parametrize("cfg", [scaled(WORKLOADS[2], 2048, Hq=8, Hkv=2, seed=61),
+                                 # past 32768 rows: the multi-block radix budget and selection, whose
+                                 # histograms the captured call clears with a kernel on every replay
+                                 scaled(WORKLOADS[2], 40001, Hq=4, Hkv=2, seed=64),
                                  Workload("graph_f32", L=300, Hq=2, Hkv=2, d=128, q=3, tau=0.02, dtype="f32",
                                           salient_frac=0.05, shared_frac=1.0, seed=62)],
-                         ids=["bf16_L2048", "f32_L300"])
+                         ids=["bf16_L2048", "bf16_L40001_multiblock", "f32_L300"])
 def test_layer_replays_bitwise(gpu, cfg):
     inp = make_layer(cfg)
     Q, K, V, X = (inp[n].to(gpu) for n in ("Q", "K", "V", "X"))
@@ -61,10 +64,14 @@ def test_layer_replays_bitwise(gpu, cfg):
         assert torch.equal(Y2, Ye), i
 
 
-def test_varlen_layer_replays_bitwise(gpu):
+@pytest.mark.parametrize("lengths", [[700, 37, 1500, 256], [40001, 300, 33000]],
+                         ids=["short", "multiblock_and_one_workgroup"])
+def test_varlen_layer_replays_bitwise(gpu, lengths):
+    """Samples past 32768 rows take the multi-block radix kernels (histograms cleared by a kernel
+    inside the captured call), the others the one-workgroup kernels."""
     cfg = Workload("graph_varlen", L=1, Hq=8, Hkv=2, d=128, q=4, tau=0.05, dtype="bf16",
                    salient_frac=0.05, shared_frac=0.5, seed=63)
-    b = make_batch(cfg, [700, 37, 1500, 256])
+    b = make_batch(cfg, lengths)
     cu = [int(v) for v in b["cu_seqlens"]]
     Q, K, V, X = (b[n].to(gpu) for n in ("Q", "K", "V", "X"))
     s = binding.shape(cu[-1], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, cfg.tau, cfg.dtype)
