@@ -81,7 +81,9 @@ int64_t tsa_capacity(int64_t L);
 /* Workspace (device memory, 256-byte aligned) needed by tsa_score, tsa_budget and tsa_select;
  * one buffer of this size serves any of them. */
 size_t tsa_stage_workspace_bytes(const tsa_shape* s);
-/* Workspace needed by tsa_layer (holds every intermediate of the layer). */
+/* Workspace needed by tsa_layer and tsa_layer_ratio: the stage workspace plus every intermediate
+ * the layer materialises (s_h, s_l, idx, inv, then Kh and Vht; f32 also Qh and Oh -- the bf16 layer
+ * reads its queries through idx and writes Y from the attention epilogue, so it needs neither). */
 size_t tsa_layer_workspace_bytes(const tsa_shape* s);
 /* Workspace needed by tsa_dense_attn_causal. */
 size_t tsa_dense_workspace_bytes(const tsa_shape* s);

@@ -76,9 +76,16 @@ def test_capacity_and_workspace_sizes():
     bad = good()
     bad.d = 96
     assert binding.layer_workspace_bytes(bad) == 0
-    # the layer workspace holds Q_hat, K_hat, V_hat and O_hat at capacity
+    # the bf16 layer reads its queries through the selection and writes Y from the attention, so its
+    # workspace holds K_hat and V_hat^T at capacity but no Q_hat or O_hat; the fp32 layer and the
+    # block-sparse layer materialise all four
     s = good()
-    assert binding.layer_workspace_bytes(s) >= 4 * 32 * binding.capacity(4096) * 128 * 2
+    comp = 32 * binding.capacity(4096) * 128 * 2
+    assert 2 * comp <= binding.layer_workspace_bytes(s) < 3 * comp
+    assert binding.layer_block_sparse_workspace_bytes(s) >= 4 * comp
+    f = good()
+    f.dtype = binding.F32
+    assert binding.layer_workspace_bytes(f) >= 4 * 2 * comp
 
 
 class FakePtr:
@@ -158,7 +165,8 @@ def test_varlen_capacity_and_validation():
     assert binding.varlen_capacity([0, 5, 5]) == -1 and binding.varlen_capacity([1, 5]) == -1
     s = binding.shape(1000, 4, 2, 128, 5, 0.05, "bf16")
     cu = [0, 37, 700, 1000]
-    assert binding.layer_varlen_workspace_bytes(s, cu) >= 4 * 128 * 2 * 4 * binding.varlen_capacity(cu)
+    comp = 4 * 128 * 2 * binding.varlen_capacity(cu)        # one compressed tensor of the batch
+    assert 2 * comp <= binding.layer_varlen_workspace_bytes(s, cu) < 3 * comp
     assert binding.dense_varlen_workspace_bytes(s, cu) >= 2 * 128 * 2 * binding.varlen_capacity(cu)
     for bad, status in (([0, 37, 700, 999], 1), ([0, 700, 37, 1000], 1), ([1, 37, 700, 1000], 1),
                         ([0, 3, 700, 1000], 2)):              # last: a sample shorter than q = 5
@@ -196,3 +204,45 @@ def test_block_sparse_host_rules():
     with pytest.raises(binding.TsaError) as e:                       # no workspace
         binding.block_select(s, 0.9, p, p, p, p, p, stream=0)
     assert e.value.status == 5
+
+
+def test_binding_validates_tensors_before_the_library():
+    """The binding refuses a tensor that would make a kernel read or write outside its buffer (wrong
+    element type, too few elements, a non-contiguous view, host memory) before libtsa sees its
+    address; these raise on the CPU, so nothing is launched."""
+    import torch
+    s = binding.shape(300, 4, 2, 64, 8, 0.05, "bf16")
+    L, Hq, Hkv, d = 300, 4, 2, 64
+    bf = lambda *sh: torch.zeros(*sh, dtype=torch.bfloat16)
+    Q, K, V, X, Y = bf(L, Hq, d), bf(L, Hkv, d), bf(L, Hkv, d), bf(L, Hq, d), bf(L, Hq, d)
+    kl = torch.zeros(2, dtype=torch.int32)
+    ws = torch.zeros(256, dtype=torch.uint8)
+
+    def status(fn, *a):
+        with pytest.raises(binding.TsaError) as e:
+            fn(*a)
+        return e.value.status, str(e.value)
+
+    st, msg = status(binding.layer, s, Q.float(), K, V, X, Y, kl, ws)            # fp32 under a bf16 shape
+    assert st == 3 and "Q" in msg
+    st, msg = status(binding.layer, s, Q, K[:-1], V, X, Y, kl, ws)               # one row short
+    assert st == 1 and "K holds" in msg
+    st, msg = status(binding.layer, s, Q, K, V, X.transpose(0, 1), Y, kl, ws)    # a strided view
+    assert st == 1 and "contiguous" in msg
+    st, msg = status(binding.layer, s, Q, K, V, X, Y, kl[:1], ws)                # {k, L'} needs two words
+    assert st == 1 and "kLp_dev" in msg
+    st, msg = status(binding.layer, s, Q, K, V, X, Y, kl, ws)                    # all well formed, on the host
+    assert st == 1 and "not a device tensor" in msg
+    s_h = torch.zeros(Hq, L)
+    st, msg = status(binding.select, s, s_h, kl[1:2], torch.zeros(Hq, L, dtype=torch.int64), None, ws)
+    assert st == 3 and "idx" in msg
+    C = binding.capacity(L)
+    Qh, Kh, Oh = bf(Hq, C, d), bf(Hq, C, d), bf(Hq, C, d)
+    st, msg = status(binding.attn_causal, s, Qh, Kh, bf(Hq, d, C - 1), kl[1:2], Oh)   # V_hat^T below capacity
+    assert st == 1 and "Vht" in msg
+    nb = binding.block_count(L)
+    st, msg = status(binding.attn_block_sparse, s, Qh, Kh, bf(Hq, d, C), kl[1:2],
+                     torch.zeros(Hq, nb, nb, dtype=torch.int32), torch.zeros(Hq, nb, dtype=torch.int32), Oh)
+    assert st == 3 and "blist" in msg
+    st, msg = status(binding.layer_varlen, s, [0, 100, 300], Q, K, V, X, Y, kl, ws)    # {k_b, L'_b} per sample
+    assert st == 1 and "kLp_dev" in msg

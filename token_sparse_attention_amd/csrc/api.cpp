@@ -53,37 +53,44 @@ size_t list_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * 
 size_t count_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * sizeof(int32_t); }
 size_t logits_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * block_count(s) * sizeof(double); }
 
-// The layer workspace = stage workspace + every intermediate tensor of the layer (+ the block
-// lists of the block-sparse variant).
+// The bf16 layer without block sparsity reads its queries through idx inside the attention and
+// writes Y from the attention's epilogue, so it never materialises Q_hat or O_hat.
+bool fused_layer(const tsa_shape* s, bool block_sparse) { return s->dtype == TSA_BF16 && !block_sparse; }
+
+// The layer workspace = stage workspace + every intermediate tensor the layer materialises (+ the
+// pooled means and block lists of the block-sparse variant).  Offsets of regions a variant does not
+// use are 0 and never read.
 struct LayerWs {
   StageWs st;
-  size_t s_h, s_l, idx, inv, Qh, Kh, Vht, Oh, total;
-  size_t qbar, kbar, zl, blist, bcnt, total_bs;
+  size_t s_h, s_l, idx, inv, Qh, Kh, Vht, Oh;
+  size_t qbar, kbar, zl, blist, bcnt, total;
 };
 
-LayerWs layer_layout(const tsa_shape* s) {
-  LayerWs w;
+LayerWs layer_layout(const tsa_shape* s, bool block_sparse) {
+  LayerWs w{};
   w.st = stage_layout(s);
   size_t o = w.st.total;
   auto take = [&](size_t n) { size_t at = o; o += up(n); return at; };
   const size_t C = (size_t)tsa_capacity(s->L);
   const size_t hl = (size_t)s->Hq * s->L;
   const size_t comp = (size_t)s->Hq * C * s->d * elem_bytes(s->dtype);
+  const bool fused = fused_layer(s, block_sparse);
   w.s_h = take(hl * sizeof(float));
   w.s_l = take((size_t)s->L * sizeof(float));
   w.idx = take(hl * sizeof(int32_t));
   w.inv = take(hl * sizeof(int32_t));
-  w.Qh = take(comp);
+  if (!fused) w.Qh = take(comp);
   w.Kh = take(comp);
   w.Vht = take(comp);
-  w.Oh = take(comp);
+  if (!fused) w.Oh = take(comp);
+  if (block_sparse) {
+    w.qbar = take(pooled_bytes(s));
+    w.kbar = take(pooled_bytes(s));
+    w.zl = take(logits_bytes(s));
+    w.blist = take(list_bytes(s));
+    w.bcnt = take(count_bytes(s));
+  }
   w.total = o;
-  w.qbar = take(pooled_bytes(s));
-  w.kbar = take(pooled_bytes(s));
-  w.zl = take(logits_bytes(s));
-  w.blist = take(list_bytes(s));
-  w.bcnt = take(count_bytes(s));
-  w.total_bs = o;
   return w;
 }
 
@@ -190,10 +197,11 @@ VarlenWs varlen_layout(const tsa_shape* s, int32_t B, const int64_t* cu) {
   w.s_l = take(P * sizeof(float));
   w.idx = take((size_t)s->Hq * P * sizeof(int32_t));
   w.inv = take((size_t)s->Hq * P * sizeof(int32_t));
-  w.Qh = take(comp);
+  const bool fused = fused_layer(s, false);
+  w.Qh = fused ? 0 : take(comp);
   w.Kh = take(comp);
   w.Vht = take(comp);
-  w.Oh = take(comp);
+  w.Oh = fused ? 0 : take(comp);
   w.total = o;
   return w;
 }
@@ -208,8 +216,8 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   TSA_TRY(opt_ptrs({X}));
   if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
   if (block_sparse && block_count(s) > kMaxKeyBlocks) return TSA_ERR_UNSUPPORTED;
-  const LayerWs w = layer_layout(s);
-  TSA_TRY(check_ws(ws, ws_bytes, block_sparse ? w.total_bs : w.total));
+  const LayerWs w = layer_layout(s, block_sparse);
+  TSA_TRY(check_ws(ws, ws_bytes, w.total));
   hipStream_t st = stream_of(stream);
   const StageWs& g = w.st;
   const int64_t C = tsa_capacity(s->L);
@@ -239,7 +247,7 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
                       at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
   // bf16 without block sparsity: the attention reads the queries through idx and writes Y itself
   // (gather of the queries and decompression folded into it); the result is bitwise the same
-  const bool fused = s->dtype == TSA_BF16 && !block_sparse;
+  const bool fused = fused_layer(s, block_sparse);
   if (e == hipSuccess)
     e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C,
                       fused ? nullptr : at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
@@ -308,7 +316,7 @@ size_t tsa_stage_workspace_bytes(const tsa_shape* s) {
 }
 
 size_t tsa_layer_workspace_bytes(const tsa_shape* s) {
-  return tsa_check_args(s) == TSA_OK ? layer_layout(s).total : 0;
+  return tsa_check_args(s) == TSA_OK ? layer_layout(s, false).total : 0;
 }
 
 size_t tsa_dense_workspace_bytes(const tsa_shape* s) {
@@ -493,7 +501,7 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
   const StageWs& g = w.st;
   const size_t eb = elem_bytes(s->dtype), Hq = s->Hq, Hkv = s->Hkv, d = s->d;
   int32_t* kLp = at<int32_t>(ws, w.kLp);
-  const bool fused = s->dtype == TSA_BF16;
+  const bool fused = fused_layer(s, false);
   std::vector<int64_t> P(B + 1, 0);
   for (int32_t b = 0; b < B; ++b) P[b + 1] = P[b] + tsa_capacity(cu_seqlens[b + 1] - cu_seqlens[b]);
   auto tok = [&](const void* base, size_t heads, int32_t b) {
@@ -559,7 +567,7 @@ size_t tsa_block_select_workspace_bytes(const tsa_shape* s) {
 }
 
 size_t tsa_layer_block_sparse_workspace_bytes(const tsa_shape* s) {
-  return tsa_check_args(s) == TSA_OK ? layer_layout(s).total_bs : 0;
+  return tsa_check_args(s) == TSA_OK ? layer_layout(s, true).total : 0;
 }
 
 int tsa_block_select(const tsa_shape* s, float gamma, const void* Qh, const void* Kh, const int32_t* Lp_dev,
