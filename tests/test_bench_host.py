@@ -125,3 +125,64 @@ def test_attention_counters_only_on_the_counted_shape_and_source(monkeypatch):
     assert bench.measured_counters(WORKLOADS[5]) is None
     monkeypatch.setattr(bench, "source_hash", lambda path: "0000000000000000")
     assert bench.measured_counters(WORKLOADS[4]) is None
+
+
+def _sweep_evidence_from_oracle(cfg, kind, **param):
+    """Evidence shaped like bench.sweep_evidence's, built from the oracle's own layer (the stored
+    output rounded to the storage type as the device writes it)."""
+    inp = make_layer(cfg)
+    f64 = lambda t: t.double().numpy()
+    Q, K, V, X = (f64(inp[n]) for n in ("Q", "K", "V", "X"))
+    tau = float(np.float32(param.get("tau", cfg.tau)))
+    if kind == "block":
+        r = oracle.block_sparse_layer(Q, K, V, X, tau, cfg.q, param["gamma"])
+    else:
+        r = oracle.layer(Q, K, V, X, tau, cfg.q, sparsity=param.get("sparsity"))
+    Lp = r["Lp"]
+    Y = oracle.round_to_storage(r["Y"], cfg.dtype)
+    rng = np.random.default_rng(3)
+    rows = {h: np.sort(rng.choice(Lp, 6, replace=False)) for h in range(cfg.Hq)}
+    ev = {"kind": kind, **param, "k_gpu": r["k"], "Lp_gpu": Lp, "sel": np.asarray(r["idx"]),
+          "rows": {h: (rw, Y[r["idx"][h][rw], h]) for h, rw in rows.items()},
+          "unselected_rows_equal_X": True, "all_rows_written": True}
+    if kind == "block":
+        ev["block_lists"] = {h: r["keep"][h] for h in range(cfg.Hq)}
+    return (Q, K, V, X), r, ev
+
+
+def test_sweep_verdict_accepts_the_oracle_and_rejects_planted_errors():
+    cfg = WORKLOADS[1]
+    for kind, param in (("tau", {"tau": 0.5}), ("ratio", {"sparsity": 0.3}), ("block", {"tau": 0.3, "gamma": 0.5})):
+        (Q, K, V, X), r, ev = _sweep_evidence_from_oracle(cfg, kind, **param)
+        v = bench.sweep_verdict(cfg, Q, K, V, X, r["s_h"], r["s_l"], ev)
+        assert v["pass"], (kind, v)
+        assert v["heads_selection_equal"] == cfg.Hq and v["output_rows_checked"] == 6 * cfg.Hq
+        # one sampled output element off by more than the tolerance
+        bad = dict(ev, rows=dict(ev["rows"]))
+        rw, y = bad["rows"][1]
+        y = y.copy()
+        y[2, 7] += 0.05
+        bad["rows"][1] = (rw, y)
+        assert not bench.sweep_verdict(cfg, Q, K, V, X, r["s_h"], r["s_l"], bad)["pass"], kind
+        # a row the layer never wrote, or a dropped token that lost its X
+        for flag in ("all_rows_written", "unselected_rows_equal_X"):
+            assert not bench.sweep_verdict(cfg, Q, K, V, X, r["s_h"], r["s_l"], dict(ev, **{flag: False}))["pass"]
+        # a keep count one off
+        assert not bench.sweep_verdict(cfg, Q, K, V, X, r["s_h"], r["s_l"], dict(ev, k_gpu=ev["k_gpu"] + 1))["pass"]
+        # a head keeping a clearly dropped token instead of its best one
+        sel = ev["sel"].copy()
+        top, low = int(np.argmax(r["s_h"][0])), int(np.argmin(r["s_h"][0]))
+        assert top in set(sel[0].tolist()) and low not in set(sel[0].tolist())
+        sel[0] = np.sort(np.array(sorted((set(sel[0].tolist()) - {top}) | {low})))
+        v = bench.sweep_verdict(cfg, Q, K, V, X, r["s_h"], r["s_l"], dict(ev, sel=sel))
+        assert not v["pass"] and v["heads_selection_equal"] == cfg.Hq - 1
+        if kind == "block":
+            # a kept-block list that drops a block the oracle keeps
+            lists = dict(ev["block_lists"])
+            h = 2
+            I = max(range(len(lists[h])), key=lambda i: len(lists[h][i]))
+            assert len(lists[h][I]) > 2
+            lists[h] = list(lists[h])
+            lists[h][I] = lists[h][I][[0, -1]]
+            v = bench.sweep_verdict(cfg, Q, K, V, X, r["s_h"], r["s_l"], dict(ev, block_lists=lists))
+            assert not v["pass"] and v["heads_block_lists_equal"] == cfg.Hq - 1

@@ -6,7 +6,12 @@ The oracle runs scoring, budget and selection in full.  Attention and the layer 
 on sampled rows, each computed one by one by the oracle: compressed rows 0-7, the last 8, rows +-1
 around every multiple of 64 and 128 up to 1024 (tile edges), and 48 seeded random rows.  Every
 row outside a head's selection must equal X bit for bit; the selections themselves are checked
-exactly against the oracle's selection on the GPU's own scores.
+exactly against the oracle's selection on the GPU's own scores.  Out-of-place layers write into a
+NaN-filled Y, so a row the kernels never wrote, in any head, shows up as a NaN.
+
+The sparsity regime of the pages (about 54% and 75% of the tokens pruned) is checked at the 128K
+shapes too: there the multi-block radix select keeps tens of thousands of tokens per head and the
+8-wave fused attention runs on a keep count far below L.
 """
 
 import numpy as np
@@ -116,9 +121,10 @@ def test_single_layer_full_size(gpu, num):
     check_scoring(cfg, inp["Q"], inp["K"], s_h, s_l, k, Lp, idx)
     ws = binding.workspace(binding.layer_workspace_bytes(s), gpu)
     kl = torch.zeros(2, dtype=torch.int32, device=gpu)
-    Y = torch.empty_like(X)
+    Y = torch.full_like(X, float("nan"))
     binding.layer(s, Q, K, V, X, Y, kl, ws)
     assert kl.tolist() == [k, Lp]
+    assert bool(torch.isfinite(Y).all())           # every row of every head written
     Y2 = torch.empty_like(X)
     binding.layer(s, Q, K, V, X, Y2, kl, ws)
     assert torch.equal(Y, Y2)                      # deterministic
@@ -164,8 +170,17 @@ def test_chain_8_layers_256k(gpu):
             print(f"[chain] layer {layer_id}: k={k} L'={Lp}", flush=True)
             check_scoring(cfg, inp["Q"], inp["K"], s_h, s_l, k, Lp, idx)
             del s_h, s_l
+            if layer_id == sparse[0]:
+                # once out of place into NaNs: every row written, and bitwise what the in-place call
+                # below leaves in X
+                Yo = torch.full_like(X, float("nan"))
+                binding.layer(s, Q, K, V, X, Yo, kl, ws)
+                assert bool(torch.isfinite(Yo).all()), layer_id
             binding.layer(s, Q, K, V, X, X, kl, ws)          # in place: Y aliases X
             assert kl.tolist() == [k, Lp]
+            if layer_id == sparse[0]:
+                assert torch.equal(Yo, X), layer_id
+                del Yo
             check_layer_output(cfg, inp, X_in, X, idx, heads=[0, 13, 18, 31], seed=layer_id)
         else:
             binding.dense_attn_causal(s, Q, K, V, X, X, dws)
@@ -181,3 +196,79 @@ def test_chain_8_layers_256k(gpu):
                 bad = np.abs(got - want) > ATOL + RTOL * np.abs(want)
                 assert not bad.any(), (layer_id, h, int(bad.sum()))
         del Q, K, V
+
+
+_C4 = {}
+
+
+def c4_inputs():
+    """The 128K workload's inputs, drawn once per test session (host tensors)."""
+    if not _C4:
+        _C4.update(make_layer(WORKLOADS[4]))
+    return _C4
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("tau", [0.5, 0.72])
+def test_sparsity_regime_full_size(gpu, tau):
+    """The 128K workload at the pages' sparsity (tau = 0.5 prunes ~54%, 0.72 ~75% of the tokens):
+    scores, budget and the multi-block selection against the oracle; the whole layer into a NaN-filled
+    Y (every row written), dropped tokens equal to X and sampled rows of ALL 32 heads within the
+    tolerance; then the block-sparse layer (gamma = 0.5) on the same selection: the kept-block lists
+    of two heads equal the oracle's and their sampled rows match."""
+    import dataclasses
+    cfg = dataclasses.replace(WORKLOADS[4], tau=tau, name=f"{WORKLOADS[4].name}_tau{tau}")
+    inp = c4_inputs()
+    print(f"\n[{cfg.name}] uploading inputs", flush=True)
+    Q, K, V, X = (inp[n].to(gpu) for n in ("Q", "K", "V", "X"))
+    s = binding.shape_of(cfg)
+    s_h, s_l, k, Lp, idx = run_stages(s, Q, K, cfg.L, cfg.Hq, gpu)
+    print(f"[{cfg.name}] k={k} L'={Lp}; checking scores, budget and selection", flush=True)
+    assert 0.4 * cfg.L > Lp > 0.2 * cfg.L if tau > 0.7 else 0.6 * cfg.L > Lp > 0.4 * cfg.L
+    check_scoring(cfg, inp["Q"], inp["K"], s_h, s_l, k, Lp, idx)
+    del s_h, s_l
+    ws = binding.workspace(binding.layer_workspace_bytes(s), gpu)
+    kl = torch.zeros(2, dtype=torch.int32, device=gpu)
+    Y = torch.full_like(X, float("nan"))
+    binding.layer(s, Q, K, V, X, Y, kl, ws)
+    assert kl.tolist() == [k, Lp]
+    assert bool(torch.isfinite(Y).all())
+    del ws
+    print(f"[{cfg.name}] checking the layer output on all {cfg.Hq} heads", flush=True)
+    check_layer_output(cfg, inp, inp["X"], Y, idx, list(range(cfg.Hq)), seed=int(100 * tau))
+
+    gamma, heads = 0.5, (3, 28)
+    lws = binding.workspace(binding.layer_block_sparse_workspace_bytes(s), gpu)
+    Y.fill_(float("nan"))
+    binding.layer_block_sparse(s, gamma, Q, K, V, X, Y, kl, lws)
+    assert kl.tolist() == [k, Lp]
+    assert bool(torch.isfinite(Y).all())
+    del lws
+    # the stage entry points' kept-block lists on the same compressed tensors
+    C, NB = binding.capacity(cfg.L), binding.block_count(cfg.L)
+    idx_t = torch.zeros(cfg.Hq, cfg.L, dtype=torch.int32)
+    idx_t[:, :Lp] = torch.from_numpy(idx.astype(np.int32))
+    Qh = torch.empty(cfg.Hq, C, cfg.d, dtype=Q.dtype, device=gpu)
+    Kh, Vht = torch.empty_like(Qh), torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=gpu)
+    binding.gather(s, Q, K, V, idx_t.to(gpu), kl[1:2], Qh, Kh, Vht)
+    blist = torch.empty(cfg.Hq, NB, NB, dtype=torch.int16, device=gpu)
+    bcnt = torch.empty(cfg.Hq, NB, dtype=torch.int32, device=gpu)
+    binding.block_select(s, gamma, Qh, Kh, kl[1:2], blist, bcnt,
+                         binding.workspace(binding.block_select_workspace_bytes(s), gpu))
+    del Qh, Kh, Vht
+    nb = -(-Lp // 128)
+    Yc = Y.cpu()
+    G = cfg.Hq // cfg.Hkv
+    print(f"[{cfg.name}] block-sparse layer: checking heads {heads}", flush=True)
+    for h in heads:
+        pos = idx[h]
+        t = torch.from_numpy(pos)
+        Qo, Ko, Vo = f64(inp["Q"][t, h]), f64(inp["K"][t, h // G]), f64(inp["V"][t, h // G])
+        keep = oracle.block_select(oracle.block_pool(Qo, Lp), oracle.block_pool(Ko, Lp), gamma)
+        got_lists = [blist[h, I, :int(bcnt[h, I])].cpu().numpy().astype(np.int64) for I in range(nb)]
+        assert all(np.array_equal(a, b) for a, b in zip(got_lists, keep)), h
+        rows = sample_rows(Lp, 300 + h)
+        want = f64(inp["X"][torch.from_numpy(pos[rows]), h]) + oracle.block_sparse_attention_rows(Qo, Ko, Vo, keep, rows)
+        got = f64(Yc[torch.from_numpy(pos[rows]), h])
+        bad = np.abs(got - want) > ATOL + RTOL * np.abs(want)
+        assert not bad.any(), ("block sparse", h, int(bad.sum()))
