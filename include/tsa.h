@@ -52,7 +52,8 @@ typedef enum {
     TSA_ERR_ALIGN = 4,        /* a tensor pointer is not 16-byte aligned */
     TSA_ERR_WORKSPACE = 5,    /* workspace NULL, misaligned (256 B) or smaller than required */
     TSA_ERR_HIP = 6,          /* a kernel launch failed */
-    TSA_ERR_UNSUPPORTED = 7   /* valid but not implemented (e.g. d not in {64, 128}) */
+    TSA_ERR_UNSUPPORTED = 7,  /* valid but not implemented (e.g. d not in {64, 128}) */
+    TSA_ERR_TOO_LARGE = 8     /* tsa_layer_noalloc: the layer's intermediates exceed its fixed scratch */
 } tsa_status;
 
 typedef enum { TSA_F32 = 0, TSA_BF16 = 1 } tsa_dtype;
@@ -139,6 +140,23 @@ int tsa_scatter_residual(const tsa_shape* s, const void* Oh, const int32_t* idx,
  * may alias X.  If kLp_dev != NULL it receives {k, L'} (device int32[2]). */
 int tsa_layer(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X,
               void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes, void* stream);
+
+/* Allocation-free tsa_layer, for callers that cannot allocate device memory at call time (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation) and cannot hold a
+ * workspace of their own.  Computes exactly what tsa_layer computes, with the same kernels, bit for
+ * bit; its intermediates live in a fixed scratch array of TSA_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory on every GPU it runs on, from the first call on that GPU until the process
+ * ends.  No call allocates or frees anything.
+ *   - The layer's workspace (tsa_layer_workspace_bytes(s)) must fit the scratch; otherwise the call
+ *     returns TSA_ERR_TOO_LARGE and enqueues nothing.  Arguments are validated as in tsa_layer.
+ *   - Every call on one GPU uses that GPU's single scratch array: calls that overlap on one GPU
+ *     (concurrent streams, or host threads sharing a device) race and give undefined results; calls
+ *     on one stream, one after another, are safe (each clears what it needs).
+ *   - The first call on a GPU looks up the array's device address with that GPU current (a host
+ *     query, not an allocation); TSA_ERR_HIP if that fails. */
+#define TSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+int tsa_layer_noalloc(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X, void* Y,
+                      int32_t* kLp_dev, void* stream);
 
 /* Fixed-ratio budget, the baseline the coverage budget is measured against in the ablations (notes,
  * "Ablations": tau = 0.005 against a fixed s = 0.3, tau = 0.010 against s = 0.5; "Key design 2"

@@ -61,7 +61,7 @@ def test_check_args_accepts_the_workloads():
 
 def test_status_strings():
     L = binding.lib()
-    for code in range(8):
+    for code in range(9):
         assert L.tsa_status_string(code).decode() == binding._STATUS[code]
     assert L.tsa_status_string(99).decode() == "unknown status"
 
@@ -246,3 +246,26 @@ def test_binding_validates_tensors_before_the_library():
     assert st == 3 and "blist" in msg
     st, msg = status(binding.layer_varlen, s, [0, 100, 300], Q, K, V, X, Y, kl, ws)    # {k_b, L'_b} per sample
     assert st == 1 and "kLp_dev" in msg
+
+
+def test_noalloc_entry_point_host_rules():
+    """The allocation-free layer validates like tsa_layer and refuses a problem whose intermediates
+    exceed its fixed scratch, both before any GPU call (these run without a GPU)."""
+    import re
+    src = open(HEADER).read()
+    m = re.search(r"#define TSA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == binding.NOALLOC_SCRATCH_BYTES
+    p = FakePtr(1 << 20)
+    s = good()
+    assert binding.layer_workspace_bytes(s) <= binding.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(binding.TsaError) as e:
+        binding.layer_noalloc(s, None, p, p, None, p, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(binding.TsaError) as e:
+        binding.layer_noalloc(s, FakePtr((1 << 20) + 4), p, p, None, p, stream=0)
+    assert e.value.status == 4
+    big = binding.shape(131072, 32, 8, 128, 16, 0.005, "bf16")
+    assert binding.layer_workspace_bytes(big) > binding.NOALLOC_SCRATCH_BYTES
+    with pytest.raises(binding.TsaError) as e:
+        binding.layer_noalloc(big, p, p, p, None, p, stream=0)
+    assert e.value.status == 8

@@ -13,7 +13,8 @@ _lib = None
 F32, BF16 = 0, 1
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "unsupported dtype",
            4: "tensor not 16-byte aligned", 5: "workspace missing, misaligned or too small",
-           6: "HIP launch failed", 7: "not implemented for these parameters"}
+           6: "HIP launch failed", 7: "not implemented for these parameters",
+           8: "intermediates exceed the fixed scratch of the allocation-free entry point"}
 
 
 class TsaError(RuntimeError):
@@ -39,6 +40,7 @@ _SIGS = {
     "tsa_attn_causal": [_P, _P, _P, _P, _P, _P],
     "tsa_scatter_residual": [_P, _P, _P, _P, _P, _P, _P],
     "tsa_layer": [_P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "tsa_layer_noalloc": [_P, _P, _P, _P, _P, _P, _P],
     "tsa_dense_attn_causal": [_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "tsa_budget_ratio": [ctypes.c_float, _P, _P, _P],
     "tsa_layer_ratio": [ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
@@ -253,6 +255,16 @@ def layer(s, Q, K, V, X, Y, kLp_dev=None, ws=None, stream=None):
     p, n = _ws(ws)
     _check("tsa_layer", lib().tsa_layer(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y),
                                         _ptr(kLp_dev), p, n, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20       # TSA_NOALLOC_SCRATCH_BYTES of tsa.h
+
+
+def layer_noalloc(s, Q, K, V, X, Y, kLp_dev=None, stream=None):
+    """tsa_layer with the library's fixed per-GPU scratch in place of a caller workspace."""
+    _validate("tsa_layer_noalloc", _layer_io(s, Q, K, V, X, Y) + [("kLp_dev", kLp_dev, _I32, 2)])
+    _check("tsa_layer_noalloc", lib().tsa_layer_noalloc(ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V), _ptr(X), _ptr(Y),
+                                                        _ptr(kLp_dev), _stream(stream)))
 
 
 def budget_ratio(s, sparsity, k_dev=None, Lp_dev=None, stream=None):

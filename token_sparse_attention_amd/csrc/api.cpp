@@ -211,10 +211,7 @@ VarlenWs varlen_layout(const tsa_shape* s, int32_t B, const int64_t* cu) {
 int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* Q, const void* K,
               const void* V, const void* X, void* Y, int32_t* kLp_dev, void* ws, size_t ws_bytes,
               void* stream, bool block_sparse = false, float gamma = 1.f) {
-  TSA_TRY(tsa_check_args(s));
-  TSA_TRY(need_ptrs({Q, K, V, Y}));
-  TSA_TRY(opt_ptrs({X}));
-  if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
+  TSA_TRY(layer_args(s, Q, K, V, X, Y, kLp_dev));
   if (block_sparse && block_count(s) > kMaxKeyBlocks) return TSA_ERR_UNSUPPORTED;
   const LayerWs w = layer_layout(s, block_sparse);
   TSA_TRY(check_ws(ws, ws_bytes, w.total));
@@ -280,6 +277,19 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
 
 }  // namespace
 
+namespace tsa {
+
+int layer_args(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X, const void* Y,
+               const int32_t* kLp_dev) {
+  TSA_TRY(tsa_check_args(s));
+  TSA_TRY(need_ptrs({Q, K, V, Y}));
+  TSA_TRY(opt_ptrs({X}));
+  if (kLp_dev && ((uintptr_t)kLp_dev & 3u)) return TSA_ERR_ALIGN;
+  return TSA_OK;
+}
+
+}  // namespace tsa
+
 extern "C" {
 
 const char* tsa_status_string(int status) {
@@ -292,6 +302,7 @@ const char* tsa_status_string(int status) {
     case TSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case TSA_ERR_HIP: return "HIP launch failed";
     case TSA_ERR_UNSUPPORTED: return "not implemented for these parameters";
+    case TSA_ERR_TOO_LARGE: return "intermediates exceed the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -5,7 +5,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tsa.h"
+
 namespace tsa {
+
+// Host validation of tsa_layer's arguments other than the workspace (status codes of tsa.h).
+int layer_args(const tsa_shape* s, const void* Q, const void* K, const void* V, const void* X, const void* Y,
+               const int32_t* kLp_dev);
 
 // Per-pass control word of a radix select over one segment (see select.hip).
 struct RadixCtl {
