@@ -83,8 +83,8 @@ int64_t tsa_capacity(int64_t L);
  * one buffer of this size serves any of them. */
 size_t tsa_stage_workspace_bytes(const tsa_shape* s);
 /* Workspace needed by tsa_layer and tsa_layer_ratio: the stage workspace plus every intermediate
- * the layer materialises (s_h, s_l, idx, inv, then Kh and Vht; f32 also Qh and Oh -- the bf16 layer
- * reads its queries through idx and writes Y from the attention epilogue, so it needs neither). */
+ * the layer materialises: s_h, s_l, idx, inv and Vht; f32 also Qh, Kh and Oh (the bf16 layer reads
+ * its query and key rows through idx and writes Y from the attention epilogue). */
 size_t tsa_layer_workspace_bytes(const tsa_shape* s);
 /* Workspace needed by tsa_dense_attn_causal. */
 size_t tsa_dense_workspace_bytes(const tsa_shape* s);

@@ -53,8 +53,9 @@ size_t list_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * 
 size_t count_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * sizeof(int32_t); }
 size_t logits_bytes(const tsa_shape* s) { return (size_t)s->Hq * block_count(s) * block_count(s) * sizeof(double); }
 
-// The bf16 layer without block sparsity reads its queries through idx inside the attention and
-// writes Y from the attention's epilogue, so it never materialises Q_hat or O_hat.
+// The bf16 layer without block sparsity reads its query and key rows through idx inside the
+// attention and writes Y from the attention's epilogue, so it never materialises Q_hat, K_hat or
+// O_hat (only V_hat^T, which the matrix cores take transposed).
 bool fused_layer(const tsa_shape* s, bool block_sparse) { return s->dtype == TSA_BF16 && !block_sparse; }
 
 // The layer workspace = stage workspace + every intermediate tensor the layer materialises (+ the
@@ -80,7 +81,7 @@ LayerWs layer_layout(const tsa_shape* s, bool block_sparse) {
   w.idx = take(hl * sizeof(int32_t));
   w.inv = take(hl * sizeof(int32_t));
   if (!fused) w.Qh = take(comp);
-  w.Kh = take(comp);
+  if (!fused) w.Kh = take(comp);
   w.Vht = take(comp);
   if (!fused) w.Oh = take(comp);
   if (block_sparse) {
@@ -199,7 +200,7 @@ VarlenWs varlen_layout(const tsa_shape* s, int32_t B, const int64_t* cu) {
   w.inv = take((size_t)s->Hq * P * sizeof(int32_t));
   const bool fused = fused_layer(s, false);
   w.Qh = fused ? 0 : take(comp);
-  w.Kh = take(comp);
+  w.Kh = fused ? 0 : take(comp);
   w.Vht = take(comp);
   w.Oh = fused ? 0 : take(comp);
   w.total = o;
@@ -242,18 +243,20 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   if (e == hipSuccess)
     e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
                       at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
-  // bf16 without block sparsity: the attention reads the queries through idx and writes Y itself
-  // (gather of the queries and decompression folded into it); the result is bitwise the same
+  // bf16 without block sparsity: the attention reads the query and key rows through idx and writes Y
+  // itself (the gather of Q and K and the decompression folded into it; only V_hat^T is gathered);
+  // the result is bitwise the same as gather -> attention -> scatter
   const bool fused = fused_layer(s, block_sparse);
   if (e == hipSuccess)
     e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C,
-                      fused ? nullptr : at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht), st);
+                      fused ? nullptr : at<void>(ws, w.Qh), fused ? nullptr : at<void>(ws, w.Kh), at<void>(ws, w.Vht),
+                      st);
   if (fused) {
     if (e == hipSuccess) e = launch_fill_unselected(s->dtype, s->d, inv, X, Y, s->L, s->Hq, st);
     if (e == hipSuccess) {
       const AttnSeqDesc one{0, 0, s->L, C, kLp + 1, idx};
-      e = launch_attention_varlen(s->dtype, s->d, false, Q, at<void>(ws, w.Kh), at<void>(ws, w.Vht), 1, &one, s->Hq,
-                                  s->Hkv, X, Y, st, true);
+      e = launch_attention_varlen(s->dtype, s->d, false, Q, K, at<void>(ws, w.Vht), 1, &one, s->Hq, s->Hkv, X, Y, st,
+                                  true);
     }
     return hip_status(e);
   }
@@ -542,7 +545,8 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
                         at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
     if (e == hipSuccess)
       e = launch_gather(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), tok(V, Hkv, b), idx, kl + 1, Lb, s->Hq,
-                        s->Hkv, Cb, fused ? nullptr : comp(w.Qh, b), comp(w.Kh, b), comp(w.Vht, b), st);
+                        s->Hkv, Cb, fused ? nullptr : comp(w.Qh, b), fused ? nullptr : comp(w.Kh, b), comp(w.Vht, b),
+                        st);
     if (fused && e == hipSuccess)
       e = launch_fill_unselected(s->dtype, s->d, inv, X ? tok(X, Hq, b) : nullptr,
                                  static_cast<char*>(Y) + (size_t)cu_seqlens[b] * Hq * d * eb, Lb, s->Hq, st);
@@ -554,8 +558,8 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
       seqs.push_back({cu_seqlens[b], P[b], cu_seqlens[b + 1] - cu_seqlens[b], P[b + 1] - P[b], kLp + 2 * b + 1,
                       at<int32_t>(ws, w.idx) + Hq * (size_t)P[b]});
     if (fused)
-      e = launch_attention_varlen(s->dtype, s->d, false, Q, at<void>(ws, w.Kh), at<void>(ws, w.Vht), B, seqs.data(),
-                                  s->Hq, s->Hkv, X, Y, st, true);
+      e = launch_attention_varlen(s->dtype, s->d, false, Q, K, at<void>(ws, w.Vht), B, seqs.data(), s->Hq, s->Hkv, X,
+                                  Y, st, true);
     else
       e = launch_attention_varlen(s->dtype, s->d, false, at<void>(ws, w.Qh), at<void>(ws, w.Kh), at<void>(ws, w.Vht),
                                   B, seqs.data(), s->Hq, s->Hkv, nullptr, at<void>(ws, w.Oh), st);

@@ -62,9 +62,10 @@ constexpr int64_t kFourHeadsMinLen = 163840;
 // Compressed: the region of sequence s in Qh, Kh, Oh is [Hq][C][d] and in Vht [Hq][d][C], starting
 // at element Hq * d * cap_off.  Dense: Q, X, Y [tokens][Hq][d], K [tokens][Hkv][d] from token
 // tok_off on; Vt [Hkv][d][C] (V transposed) from element Hkv * d * cap_off on.  Fused compressed
-// (gather of the queries and decompression folded in): Kh, Vht as compressed; query row i of head h
-// is Q[tok_off + idx[h][i]][h] and its output goes to Y at that same row, plus X when given, after
-// rounding to the storage type as the separate decompression would.
+// (the gather of Q and K and the decompression folded in): Q and K are the uncompressed [tokens][Hq][d]
+// and [tokens][Hkv][d] inputs, query row i and key row j of head h are Q[tok_off + idx[h][i]][h] and
+// K[tok_off + idx[h][j]][g]; Vht as compressed; the output of row i goes to Y at token idx[h][i],
+// plus X when given, after rounding to the storage type as the separate decompression would.
 struct AttnArgs {
   const void* Q;
   const void* K;
@@ -133,9 +134,24 @@ __host__ __device__ __forceinline__ void dma_1k(const void* base, uint32_t bytes
 #endif
 }
 
-template <int D, bool DENSE, bool SPARSE, bool FUSED, int NW>
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// N direct loads of 1 KiB each into LDS at lds + 1024*i, lane l's 16 bytes coming from its own
+// 64-bit address src[i] (rows gathered through an index, beyond the reach of 32-bit buffer
+// offsets).  As dma_1k, compiled in the device pass only.
+template <int N>
+__host__ __device__ __forceinline__ void dma_1k_gather(char* lds, const char* const (&src)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src[i], (lds_void_t*)(lds + 1024 * i), 16, 0, 0);
+#endif
+}
+
+template <int D, bool DENSE, bool SPARSE, bool FUSED, int NW, bool WIDE = false>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) {
   static_assert(!SPARSE || NW == 4, "block-sparse lists are per 128 query rows");
+  static_assert(!WIDE || FUSED, "64-bit row addressing is for key rows gathered through idx");
   constexpr int NT = 64 * NW;           // threads
   constexpr int BM = 32 * NW, BN = 64;
   constexpr int KS = D / 16;            // K-steps of 16 over the head dim (score product)
@@ -167,7 +183,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
   // element offsets of this (sequence, head) in Q/O, K and V^T
   const size_t qo_off = (DENSE || FUSED) ? ((size_t)sg.tok_off * a.Hq + h) * D
                                          : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
-  const size_t k_off = DENSE ? ((size_t)sg.tok_off * a.Hkv + g) * D : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
+  const size_t k_off = (DENSE || FUSED) ? ((size_t)sg.tok_off * a.Hkv + g) * D
+                                        : ((size_t)sg.cap_off * a.Hq + (size_t)h * C) * D;
   const size_t v_off = (size_t)sg.cap_off * (DENSE ? a.Hkv : a.Hq) * D + (size_t)(DENSE ? g : h) * D * C;
   const char* qbase = static_cast<const char*>(a.Q) + qo_off * 2;
   const char* kbase = static_cast<const char*>(a.K) + k_off * 2;
@@ -208,22 +225,57 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
   auto kswz = [](int m) { return KROW == 256 ? (m & 15) : ((m ^ ((m >> 3) & 1)) & 7); };
   auto vswz = [](int r) { return (r ^ ((r >> 3) & 1)) & 7; };
 
-  // direct-load sources: lane offsets of the chunk each lane brings into its 16-byte LDS slot
-  uint32_t voffK[KDMA], voffV[VDMA];
+  // direct-load sources: the tile row and the byte offset within that row of the chunk each lane
+  // brings into its 16-byte LDS slot, and (V^T) the lane's offset within the tile
+  int krow[KDMA];
+  uint32_t kchunk[KDMA], voffV[VDMA];
 #pragma unroll
   for (int i = 0; i < KDMA; ++i) {
     const int o = (w * KDMA + i) * 1024 + 16 * lane, m = o / KROW, c = ((o % KROW) / 16) ^ kswz(m);
-    voffK[i] = (uint32_t)perm(m) * k_rs + (uint32_t)c * 16u;
+    krow[i] = perm(m);
+    kchunk[i] = (uint32_t)c * 16u;
   }
 #pragma unroll
   for (int i = 0; i < VDMA; ++i) {
     const int o = (w * VDMA + i) * 1024 + 16 * lane, r = o / VROW, c = ((o % VROW) / 16) ^ vswz(r);
     voffV[i] = (uint32_t)r * v_rs + (uint32_t)c * 16u;
   }
+  // Fused: the K rows come straight from K [tokens][Hkv][d] through idx, so K_hat is never written.
+  // The tokens of a tile's rows are read from idx one tile ahead of their loads, through a buffer
+  // over the tile's rows that ends at row L' (the tile starts below L'): rows at or past L' read
+  // token 0, a valid row whose key follows every valid query, so the causal mask gives it weight
+  // exactly 0.  Row offsets are 32-bit buffer offsets while K spans less than 4 GiB from the
+  // sequence's first token, 64-bit addresses (WIDE) otherwise.
+  const uint32_t tok_rs = (uint32_t)a.Hkv * D * 2;   // bytes between consecutive tokens' K rows
+  const int32_t* hidx = FUSED ? sg.idx + (size_t)h * sg.L : nullptr;
+  const uint32_t k_extent = FUSED && !WIDE ? (uint32_t)(sg.L - 1) * tok_rs + D * 2 : 0u;
+  auto ktok = [&](int kb, int (&tk)[KDMA]) {
+    const int key0 = kb * BN;
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(hidx + key0, (uint32_t)(Lp - key0) * 4u);
+#pragma unroll
+    for (int i = 0; i < KDMA; ++i) tk[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)krow[i] * 4u, 0, 0);
+  };
+  int tk_next[KDMA];                    // fused: tokens of the next K tile to load
   auto dma_k = [&](int kb, int slot) {
-    const int key0 = kb * BN, nval = Lp - key0 < BN ? Lp - key0 : BN;
-    // K rows at or beyond L' fall outside the range and arrive as zeros
-    dma_1k<KDMA>(kbase + (size_t)key0 * k_rs, (uint32_t)(nval - 1) * k_rs + D * 2, smem + slot * KTILE + w * KDMA * 1024, voffK);
+    char* dst = smem + slot * KTILE + w * KDMA * 1024;
+    if constexpr (FUSED && WIDE) {
+      const char* src[KDMA];
+#pragma unroll
+      for (int i = 0; i < KDMA; ++i) src[i] = kbase + (size_t)(uint32_t)tk_next[i] * tok_rs + kchunk[i];
+      dma_1k_gather<KDMA>(dst, src);
+    } else if constexpr (FUSED) {
+      uint32_t voff[KDMA];
+#pragma unroll
+      for (int i = 0; i < KDMA; ++i) voff[i] = __umul24((uint32_t)tk_next[i], tok_rs) + kchunk[i];
+      dma_1k<KDMA>(kbase, k_extent, dst, voff);
+    } else {
+      const int key0 = kb * BN, nval = Lp - key0 < BN ? Lp - key0 : BN;
+      uint32_t voff[KDMA];
+#pragma unroll
+      for (int i = 0; i < KDMA; ++i) voff[i] = (uint32_t)krow[i] * k_rs + kchunk[i];
+      // K rows at or beyond L' fall outside the range and arrive as zeros
+      dma_1k<KDMA>(kbase + (size_t)key0 * k_rs, (uint32_t)(nval - 1) * k_rs + D * 2, dst, voff);
+    }
   };
   auto dma_v = [&](int kb, int slot) {
     dma_1k<VDMA>(vbase + (size_t)kb * BN * 2, (uint32_t)(D - 1) * v_rs + BN * 2, smem + 2 * KTILE + slot * VTILE + w * VDMA * 1024, voffV);
@@ -252,9 +304,16 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
     }
   };
 
+  if constexpr (FUSED) ktok(0, tk_next);
   dma_k(ktile(0), 0);
   dma_v(ktile(0), 0);
-  if (nkb > 1) dma_k(ktile(1), 1);
+  if (nkb > 1) {
+    if constexpr (FUSED) ktok(1, tk_next);
+    dma_k(ktile(1), 1);
+  }
+  if constexpr (FUSED) {                // tokens of K(2), consumed by tile 0
+    if (nkb > 2) ktok(2, tk_next);
+  }
   TSA_WAIT_VMEM();
   __syncthreads();
   f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
@@ -269,6 +328,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
     const char* vslot = smem + 2 * KTILE + P * VTILE;
     if (kb + 2 < nkb) dma_k(ktile(kb + 2), P);
     if (kb + 1 < nkb) dma_v(ktile(kb + 1), P ^ 1);
+    if constexpr (FUSED) {              // tokens of K(kb + 3), waited for with this tile's loads
+      if (kb + 3 < nkb) ktok(kb + 3, tk_next);
+    }
     const int key0 = ktile(kb) * BN, nval = Lp - key0;
     if (nval < BN) {                    // last tile: zero the V^T columns at and beyond L'
       for (int e = tid; e < D * (BN - nval); e += NT) {
@@ -486,10 +548,20 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 template <int D, bool DENSE, bool SPARSE = false, bool FUSED = false>
-static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st, int nw = kAttnWaves) {
+static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st, int nw = kAttnWaves,
+                           bool wide = false) {
   if (dtype == 1) {
     if constexpr (SPARSE) {
       attn_bf16_kernel<D, DENSE, SPARSE, FUSED, 4><<<(unsigned)nblocks, 256, 0, st>>>(a);
+    } else if constexpr (FUSED) {
+      // key rows gathered through idx: 32-bit buffer offsets while K spans less than 4 GiB
+      if (wide) {
+        if (nw == 4) attn_bf16_kernel<D, false, false, true, 4, true><<<(unsigned)nblocks, 256, 0, st>>>(a);
+        else attn_bf16_kernel<D, false, false, true, kAttnWaves, true><<<(unsigned)nblocks, 64 * kAttnWaves, 0, st>>>(a);
+      } else {
+        if (nw == 4) attn_bf16_kernel<D, false, false, true, 4><<<(unsigned)nblocks, 256, 0, st>>>(a);
+        else attn_bf16_kernel<D, false, false, true, kAttnWaves><<<(unsigned)nblocks, 64 * kAttnWaves, 0, st>>>(a);
+      }
     } else {
       if (nw == 4) attn_bf16_kernel<D, DENSE, SPARSE, FUSED, 4><<<(unsigned)nblocks, 256, 0, st>>>(a);
       else attn_bf16_kernel<D, DENSE, SPARSE, FUSED, kAttnWaves><<<(unsigned)nblocks, 64 * kAttnWaves, 0, st>>>(a);
@@ -512,6 +584,8 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
     int64_t longest = 0;
     for (int i = 0; i < a.nseg; ++i) longest = seqs[first + i].L > longest ? seqs[first + i].L : longest;
     const int nw = longest <= kShortMaxLen ? 4 : kAttnWaves;
+    // a sequence's K rows span L * Hkv * d * 2 bytes from its first token
+    const bool wide = (uint64_t)longest * (uint64_t)Hkv * (uint64_t)d * 2u >= (uint64_t(1) << 32);
     const int bm = dtype == 1 ? 32 * nw : 64;      // query rows per block
     int nblocks = 0;
     for (int i = 0; i < a.nseg; ++i) {
@@ -525,8 +599,8 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
     }
     hipError_t e;
     if (fused)
-      e = d == 128 ? run_attn<128, false, false, true>(dtype, a, nblocks, st, nw)
-                   : run_attn<64, false, false, true>(dtype, a, nblocks, st, nw);
+      e = d == 128 ? run_attn<128, false, false, true>(dtype, a, nblocks, st, nw, wide)
+                   : run_attn<64, false, false, true>(dtype, a, nblocks, st, nw, wide);
     else if (d == 128)
       e = dense ? run_attn<128, true>(dtype, a, nblocks, st, nw) : run_attn<128, false>(dtype, a, nblocks, st, nw);
     else

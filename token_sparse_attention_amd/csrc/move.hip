@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
     if (r < n) {
       const int64_t t = idx[(size_t)h * L + i0 + r];
       const size_t dst = ((size_t)h * C + i0 + r) * VPR + c;
-      if (Qh4) st_stream(ld_stream(&Q4[((size_t)t * Hq + h) * VPR + c]), &Qh4[dst]);   // the fused layer reads Q in place
-      st_stream(K4[((size_t)t * Hkv + g) * VPR + c], &Kh4[dst]);
+      if (Qh4) st_stream(ld_stream(&Q4[((size_t)t * Hq + h) * VPR + c]), &Qh4[dst]);   // the fused layer reads Q
+      if (Kh4) st_stream(K4[((size_t)t * Hkv + g) * VPR + c], &Kh4[dst]);               // and K in place
       v = V4[((size_t)t * Hkv + g) * VPR + c];
     }
     stage[e] = v;
@@ -100,8 +100,8 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __rest
     if (i < Lp) {
       const int64_t t = idx[(size_t)h * L + i];
       const size_t dst = ((size_t)h * C + i) * VPR + c;
-      if (Qh4) st_stream(ld_stream(&Q4[((size_t)t * Hq + h) * VPR + c]), &Qh4[dst]);   // the fused layer reads Q in place
-      st_stream(K4[((size_t)t * Hkv + g) * VPR + c], &Kh4[dst]);
+      if (Qh4) st_stream(ld_stream(&Q4[((size_t)t * Hq + h) * VPR + c]), &Qh4[dst]);   // the fused layer reads Q
+      if (Kh4) st_stream(K4[((size_t)t * Hkv + g) * VPR + c], &Kh4[dst]);               // and K in place
       x = V4[((size_t)t * Hkv + g) * VPR + c];
     }
     v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;

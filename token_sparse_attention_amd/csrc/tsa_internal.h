@@ -95,9 +95,10 @@ hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const v
 // [Hq][d][C] start at element Hq*d*cap_off, L' is read from Lp_dev, and L bounds the grid (L' <= L).
 // Dense: tokens [tok_off, tok_off + L) of Q/K/X/Y; its Vt region [Hkv][d][C] starts at element
 // Hkv*d*cap_off.  Longer sequences listed first are scheduled first.
-// Fused (compressed, bf16): Q is the uncompressed [tokens][Hq][d] input, query row i of head h is
-// token tok_off + idx[h][i] (idx [Hq][L] per sequence), and the output row is written to O (= Y)
-// at that token, plus X when given, rounded as tsa_scatter_residual rounds; Kh/Vht as compressed.
+// Fused (compressed, bf16): Q and K are the uncompressed [tokens][Hq][d] and [tokens][Hkv][d] inputs,
+// query and key row i of head h are token tok_off + idx[h][i] (idx [Hq][L] per sequence), and the
+// output row is written to O (= Y) at that token, plus X when given, rounded as tsa_scatter_residual
+// rounds; Vht as compressed.
 struct AttnSeqDesc {
   int64_t tok_off, cap_off, L, C;
   const int32_t* Lp_dev;
