@@ -179,31 +179,31 @@ static hipError_t run_score(const void* Q, const void* K, int64_t L, int Hq, int
 // ---- bf16 path on the matrix cores ---------------------------------------------------------------
 // Logits z = <Q[p][h], K[t][g]> come from v_mfma_f32_32x32x16_bf16 (bf16 products are exact in
 // float32; only the accumulation rounds).  The recent-query rows of a KV group are staged in LDS,
-// each head's q rows padded to 16 (q <= 16) or to a multiple of 32, the group to a multiple of 32.
-// A wave owns 64 keys (two blocks of 32) of each 256-key sub-chunk; a workgroup walks nsub
-// sub-chunks of one KV group.  The product is oriented so that every reduction is lane-local:
-//   pass 1: D = K Q^T, a lane holds 16 keys of ONE row: it keeps that row's running (max, sum of
-//           exponentials) in registers over all of the workgroup's keys; the two lanes sharing a
-//           row and the four waves are merged once at the end, one (max, sum) partial per row and
-//           workgroup;
-//   pass 2: D = Q K^T, a lane holds 16 rows of ONE key: the weights exp(z - m) / Z are summed over
-//           the head's rows in the lane, plus one exchange with the lane holding the other rows.
+// each head's q rows padded to 16 (q <= 16) or to a multiple of 32, the group to a multiple of 32
+// (MB blocks of 32 rows, a template parameter so the row loops unroll).  A wave owns 64 keys (two
+// blocks of 32) of each 256-key sub-chunk; a workgroup walks nsub sub-chunks of one KV group.  The
+// product is oriented so that every reduction is lane-local:
+//   pass 1: D = K Q^T, a lane holds 16 keys of ONE row: it keeps that row's (reference R, sum of
+//           exp2((z - R) c)) in registers over all of the workgroup's keys; the two lanes sharing a
+//           row and the four waves are merged once at the end, one (R, Z) partial per row and
+//           workgroup.  R is the first visible logit block's maximum and is raised only when a
+//           logit exceeds it by more than kRaise / c (2^32 in weight), so every exponential stays
+//           far from overflow and the (float64) rescale of the sum is rare;
+//   pass 2: D = Q K^T, a lane holds 16 rows of ONE key: the weights exp2((z - m) c) / Z are summed
+//           over the head's rows in the lane, plus one exchange with the lane holding the other
+//           rows.
 // Causal masks are applied only in workgroups that reach the recent window.  Every exponential is
-// exp2 of z * log2(e) / sqrt(d) - m * log2(e) / sqrt(d), formed with one float64 fma from the float32
-// logit, evaluated as exp2f(hi) * (1 + lo * ln 2) with hi + lo that argument; all sums are float64:
-// about 1e-7 relative, far inside the selection's 1e-6 tie band.
+// v_exp_f32 of a float32 argument (z - R) * c, with c split into a float32 pair (c_hi + c_lo) so
+// the product rounds once; 16 weights are summed pairwise in float32 and those sums in float64.  The
+// relative error of a score stays within a few 1e-7, inside the selection's 1e-6 tie band.
 constexpr int kMSub = 256, kMRows = 256;   // keys per sub-chunk (a block walks nsub of them); max rows
+constexpr float kRaise = 32.f;             // pass 1 raises its reference past this many log2 units
+// Masked logits: finite, so (z - R) * c stays finite whatever the sign of c's low part (an infinite
+// z would meet an infinity of the other sign in the split product), and its exponential is exactly 0
+constexpr float kMasked = -1e30f;
 
 typedef __bf16 bf16x8s_t __attribute__((ext_vector_type(8)));
 typedef float f32x16s_t __attribute__((ext_vector_type(16)));
-
-// exp2(z * c - mc) with the argument formed in float64
-__device__ __forceinline__ double exp2_mc(float z, double c, double mc) {
-  const double y = fma((double)z, c, -mc);
-  const float hi = (float)y;
-  const float lo = (float)(y - (double)hi);
-  return (double)(__builtin_amdgcn_exp2f(hi) * fmaf(lo, 0.69314718055994531f, 1.0f));
-}
 
 // The fragments of one key row (`key`, zeros past L) as the matrix-core operand wants them: lane
 // half hf holds the 8 consecutive head-dim elements 16 ks + 8 hf of slice ks.
@@ -233,92 +233,101 @@ __device__ __forceinline__ void stage_queries(const uint16_t* __restrict__ Q, ui
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void score_p1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+// exp2((z - R) * c) for a logit z, c = c_hi + c_lo (kMasked gives exactly 0)
+__device__ __forceinline__ float exp2_rel(float z, float R, float c_hi, float c_lo) {
+  const float d = z - R;
+  return __builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
+}
+
+// pairwise float32 sum of v[lo .. lo + n)
+template <int N>
+__device__ __forceinline__ float pair_sum(const float* v) {
+  if constexpr (N == 1) return v[0];
+  else return pair_sum<N / 2>(v) + pair_sum<N / 2>(v + N / 2);
+}
+
+template <int D, int MB>
+__global__ __launch_bounds__(256, MB <= 2 ? 4 : 3) void score_p1_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                        int64_t L, int Hq, int Hkv, int q, int qp, int nsub, double c,
                                                        double2* __restrict__ part) {
-  constexpr int KST = D / 16;
+  constexpr int KST = D / 16, Rp = 32 * MB;
   extern __shared__ __attribute__((aligned(16))) char score_smem[];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int G = Hq / Hkv, Rp = (G * qp + 31) / 32 * 32, MB = Rp / 32;
+  const int G = Hq / Hkv;
   uint16_t* qs = reinterpret_cast<uint16_t*>(score_smem);
   double* wz = reinterpret_cast<double*>(score_smem + (size_t)Rp * D * 2);   // [4][Rp]
   float* wm = reinterpret_cast<float*>(wz + 4 * Rp);                         // [4][Rp]
   stage_queries<D>(Q, qs, L, Hq, g, G, q, qp, Rp);
   __syncthreads();
 
+  const float c_hi = (float)c, c_lo = (float)(c - (double)c_hi), raise = kRaise / c_hi;
   const int64_t bkeys = (int64_t)nsub * kMSub;
   // every key of the workgroup precedes every recent query: no causal mask
   const bool open = (int64_t)(blockIdx.x + 1) * bkeys <= L - q + 1;
-  float M[kMRows / 32];
-  double S[kMRows / 32];
+  float R[MB];
+  double S[MB];
 #pragma unroll
-  for (int mb = 0; mb < kMRows / 32; ++mb) {
-    M[mb] = -INFINITY;
+  for (int mb = 0; mb < MB; ++mb) {
+    R[mb] = -INFINITY;
     S[mb] = 0.0;
   }
-  // the wave's key blocks of 32, jb = 2 sub + kb; the next block's fragments load during this one's math
-  bf16x8s_t kn[KST];
-  load_key_block<D>(K, L, Hkv, g, (int64_t)blockIdx.x * bkeys + 64 * w + l32, hf, kn);
+  // the wave's key blocks of 32, jb = 2 sub + kb; the next block's fragments are loaded into the same
+  // registers as soon as the current block's last product has been issued, so the loads run under
+  // the exponentials (and the other waves of the SIMD)
+  auto key_of = [&](int jb) { return (int64_t)blockIdx.x * bkeys + (jb >> 1) * kMSub + 64 * w + 32 * (jb & 1); };
+  bf16x8s_t kf[KST];
+  load_key_block<D>(K, L, Hkv, g, key_of(0) + l32, hf, kf);
 #pragma unroll 1
   for (int jb = 0; jb < 2 * nsub; ++jb) {
-    {
-      // z[r] below is key kbase + 8 (r / 4) + 4 hf + r % 4 of the lane's row
-      const int64_t kbase = (int64_t)blockIdx.x * bkeys + (jb >> 1) * kMSub + 64 * w + 32 * (jb & 1);
-      bf16x8s_t kf[KST];
+    // z[r] below is key kbase + 8 (r / 4) + 4 hf + r % 4 of the lane's row
+    const int64_t kbase = key_of(jb);
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) kf[ks] = kn[ks];
-      if (jb + 1 < 2 * nsub)
-        load_key_block<D>(K, L, Hkv, g, (int64_t)blockIdx.x * bkeys + ((jb + 1) >> 1) * kMSub + 64 * w + 32 * ((jb + 1) & 1) + l32,
-                          hf, kn);
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = 32 * mb + l32;
+      f32x16s_t z = {};
 #pragma unroll
-      for (int mb = 0; mb < kMRows / 32; ++mb) {
-        if (mb >= MB) break;
-        const int row = 32 * mb + l32, j = row / qp, i = row % qp;
+      for (int ks = 0; ks < KST; ++ks)
+        z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], *reinterpret_cast<const bf16x8s_t*>(&qs[qslot<D>(row, 2 * ks + hf)]),
+                                                    z, 0, 0, 0);
+      if (mb == MB - 1 && jb + 1 < 2 * nsub) load_key_block<D>(K, L, Hkv, g, key_of(jb + 1) + l32, hf, kf);
+      if (!open) {
         // keys kbase + rel with rel <= lim are visible to this lane's row (none for padding rows)
+        const int j = row / qp, i = row % qp;
         int lim = -1;
         if (j < G && i < q) {
-          const int64_t last = open ? kbase + 63 : L - q + i;     // the row's last visible key
+          const int64_t last = L - q + i;                        // the row's last visible key
           lim = (int)(last - kbase < 63 ? (last - kbase < -1 ? -1 : last - kbase) : 63);
         }
-        bf16x8s_t qf[KST];
 #pragma unroll
-        for (int ks = 0; ks < KST; ++ks) qf[ks] = *reinterpret_cast<const bf16x8s_t*>(&qs[qslot<D>(row, 2 * ks + hf)]);
-        f32x16s_t z = {};
-#pragma unroll
-        for (int ks = 0; ks < KST; ++ks) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], z, 0, 0, 0);
-        // masked logits become -1e30: their exponential below is exactly 0 (with a finite argument)
-        float zm = -1e30f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          z[r] = 8 * (r >> 2) + 4 * hf + (r & 3) <= lim ? z[r] : -1e30f;
-          zm = fmaxf(zm, z[r]);
-        }
-        if (zm > -1e29f) {                   // some key visible
-          const float mn = fmaxf(M[mb], zm);
-          const double mc = (double)mn * c;
-          double acc = 0.0;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc += exp2_mc(z[r], c, mc);
-          const double f = M[mb] > -INFINITY ? exp2_mc(M[mb], c, mc) : 0.0;
-          S[mb] = S[mb] * f + acc;
-          M[mb] = mn;
-        }
+        for (int r = 0; r < 16; ++r) z[r] = 8 * (r >> 2) + 4 * hf + (r & 3) <= lim ? z[r] : kMasked;
       }
+      float zm = z[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) zm = fmaxf(zm, z[r]);
+      if (zm > 0.1f * kMasked) {              // some key visible
+        if (zm > R[mb] + raise) {             // first visible block, or a logit far above the reference
+          if (R[mb] > -INFINITY) S[mb] *= exp2(((double)R[mb] - (double)zm) * c);
+          R[mb] = zm;
+        }
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = exp2_rel(z[r], R[mb], c_hi, c_lo);
+        S[mb] += (double)pair_sum<16>(e);
+      }
+      // one row block at a time: keeps a single block's accumulators and fragments live
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   // the two lanes of a row, then the four waves
 #pragma unroll
-  for (int mb = 0; mb < kMRows / 32; ++mb) {
-    if (mb >= MB) break;
-    const float m2 = __shfl_xor(M[mb], 32, kWave);
+  for (int mb = 0; mb < MB; ++mb) {
+    const float m2 = __shfl_xor(R[mb], 32, kWave);
     const double s2 = __shfl_xor(S[mb], 32, kWave);
-    const float mn = fmaxf(M[mb], m2);
+    const float mn = fmaxf(R[mb], m2);
     double Z = 0.0;
     if (mn > -INFINITY) {
-      const double mc = (double)mn * c;
-      if (M[mb] > -INFINITY) Z += S[mb] * exp2_mc(M[mb], c, mc);
-      if (m2 > -INFINITY) Z += s2 * exp2_mc(m2, c, mc);
+      if (R[mb] > -INFINITY) Z += S[mb] * exp2(((double)R[mb] - (double)mn) * c);
+      if (m2 > -INFINITY) Z += s2 * exp2(((double)m2 - (double)mn) * c);
     }
     if (hf == 0) {
       wm[w * Rp + 32 * mb + l32] = mn;
@@ -341,81 +350,86 @@ __global__ __launch_bounds__(256) void score_p1_kernel(const uint16_t* __restric
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 2) void score_p2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+template <int D, int MB>
+__global__ __launch_bounds__(256, MB <= 2 ? 4 : 3) void score_p2_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                        int64_t L, int Hq, int Hkv, int q, int qp, int nsub, double c,
                                                        const double2* __restrict__ rowstat, float* __restrict__ s_h) {
-  constexpr int KST = D / 16;
+  constexpr int KST = D / 16, Rp = 32 * MB;
   extern __shared__ __attribute__((aligned(16))) char score_smem[];
   const int g = blockIdx.y, tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hf = lane >> 5;
-  const int G = Hq / Hkv, Rp = (G * qp + 31) / 32 * 32, MB = Rp / 32;
+  const int G = Hq / Hkv;
   uint16_t* qs = reinterpret_cast<uint16_t*>(score_smem);
-  double2* rc = reinterpret_cast<double2*>(score_smem + (size_t)Rp * D * 2);   // per row: m * c, 1 / Z
+  float2* rc = reinterpret_cast<float2*>(score_smem + (size_t)Rp * D * 2);   // per row: m, 1 / Z
   stage_queries<D>(Q, qs, L, Hq, g, G, q, qp, Rp);
   for (int r = tid; r < Rp; r += 256) {
     const double2 ms = rowstat[(size_t)g * Rp + r];
     const bool ok = r / qp < G && r % qp < q && ms.x > -INFINITY;
-    rc[r] = ok ? make_double2(ms.x * c, ms.y) : make_double2(0.0, 0.0);   // 1 / Z = 0: no such row
+    rc[r] = ok ? make_float2((float)ms.x, (float)ms.y) : make_float2(0.f, 0.f);   // 1 / Z = 0: no such row
   }
   __syncthreads();
 
+  const float c_hi = (float)c, c_lo = (float)(c - (double)c_hi);
   const int64_t bkeys = (int64_t)nsub * kMSub;
   // key chunks in reverse order: pass 1 streamed K front to back, so its tail is what the
   // last-level cache still holds
   const int64_t kblk = (int64_t)gridDim.x - 1 - blockIdx.x;
   const bool open = (kblk + 1) * bkeys <= L - q + 1;
-  // the wave's key blocks of 32, jb = 2 sub + kb; the next block's fragments load during this one's math
-  bf16x8s_t kn[KST];
-  load_key_block<D>(K, L, Hkv, g, kblk * bkeys + 64 * w + l32, hf, kn);
+  // this lane's key in block jb; as in pass 1, the next block's fragments load into the same
+  // registers once the current block's last product has been issued
+  auto key_of = [&](int jb) { return kblk * bkeys + (jb >> 1) * kMSub + 64 * w + 32 * (jb & 1) + l32; };
+  bf16x8s_t kf[KST];
+  load_key_block<D>(K, L, Hkv, g, key_of(0), hf, kf);
 #pragma unroll 1
   for (int jb = 0; jb < 2 * nsub; ++jb) {
-    {
-      // this lane's key and its fragments
-      const int64_t key = kblk * bkeys + (jb >> 1) * kMSub + 64 * w + 32 * (jb & 1) + l32;
-      bf16x8s_t kf[KST];
+    const int64_t key = key_of(jb);
+    // visible to recent query i iff key - (L - q) <= i (always in workgroups before the window)
+    const int64_t kr64 = key - (L - q);
+    const int kr = open ? -1 : (int)(kr64 < -1 ? -1 : (kr64 > 1 << 20 ? 1 << 20 : kr64));
+    double hsA = 0.0, hsB = 0.0;            // the current head's rows (qp = 16: two heads)
 #pragma unroll
-      for (int ks = 0; ks < KST; ++ks) kf[ks] = kn[ks];
-      if (jb + 1 < 2 * nsub)
-        load_key_block<D>(K, L, Hkv, g, kblk * bkeys + ((jb + 1) >> 1) * kMSub + 64 * w + 32 * ((jb + 1) & 1) + l32,
-                          hf, kn);
-      // visible to recent query i iff key - (L - q) <= i (always in workgroups before the window)
-      const int64_t kr64 = key - (L - q);
-      const int kr = open ? -1 : (int)(kr64 < -1 ? -1 : (kr64 > 1 << 20 ? 1 << 20 : kr64));
-      double csA = 0.0, csB = 0.0;              // the current head's rows (qp = 16: two heads)
-#pragma unroll 1
-      for (int mb = 0; mb < MB; ++mb) {
-        bf16x8s_t qf[KST];
+    for (int mb = 0; mb < MB; ++mb) {
+      f32x16s_t z = {};
 #pragma unroll
-        for (int ks = 0; ks < KST; ++ks)
-          qf[ks] = *reinterpret_cast<const bf16x8s_t*>(&qs[qslot<D>(32 * mb + l32, 2 * ks + hf)]);
-        f32x16s_t z = {};
+      for (int ks = 0; ks < KST; ++ks)
+        z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8s_t*>(&qs[qslot<D>(32 * mb + l32, 2 * ks + hf)]),
+                                                    kf[ks], z, 0, 0, 0);
+      if (mb == MB - 1 && jb + 1 < 2 * nsub) load_key_block<D>(K, L, Hkv, g, key_of(jb + 1), hf, kf);
+      // z[r]: row 32 mb + 8 (r / 4) + 4 hf + r % 4 (its constants are LDS broadcasts: every lane
+      // of a half reads the same row), recent-query index ibase + that offset (qp = 16: mod 16)
+      const int ibase = qp == 16 ? 0 : (32 * mb) % qp;
+      float wgt[16];
 #pragma unroll
-        for (int ks = 0; ks < KST; ++ks) z = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[ks], kf[ks], z, 0, 0, 0);
-        // z[r]: row 32 mb + 8 (r / 4) + 4 hf + r % 4 (its constants are LDS broadcasts: every lane
-        // of a half reads the same row), recent-query index ibase + that offset (qp = 16: mod 16)
-        const int ibase = qp == 16 ? 0 : (32 * mb) % qp;
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int off0 = 8 * r4 + 4 * hf;
+        const float4 c01 = *reinterpret_cast<const float4*>(&rc[32 * mb + off0]);
+        const float4 c23 = *reinterpret_cast<const float4*>(&rc[32 * mb + off0 + 2]);
+        const float mr[4] = {c01.x, c01.z, c23.x, c23.z}, iz[4] = {c01.y, c01.w, c23.y, c23.w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 8 * (r >> 2) + 4 * hf + (r & 3);
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * r4 + u, off = off0 + u;
           const int i = qp == 16 ? off - 16 * (r >> 3) : ibase + off;
-          const double2 rcr = rc[32 * mb + off];
-          const float zv = kr <= i ? z[r] : -1e30f;             // masked: weight exactly 0
-          const double wgt = exp2_mc(zv, c, rcr.x) * rcr.y;
-          if (qp == 16 && r >= 8) csB += wgt;
-          else csA += wgt;
-        }
-        if (qp == 16 || (32 * (mb + 1)) % qp == 0) {     // the block ends a head (qp = 16: two)
-          const int jA = qp == 16 ? 2 * mb : (32 * mb) / qp;
-          const double a = csA + __shfl_xor(csA, 32, kWave);
-          if (hf == 0 && key < L && jA < G) s_h[(size_t)(g * G + jA) * L + key] = (float)a;
-          if (qp == 16) {
-            const double bsum = csB + __shfl_xor(csB, 32, kWave);
-            if (hf == 0 && key < L && jA + 1 < G) s_h[(size_t)(g * G + jA + 1) * L + key] = (float)bsum;
-          }
-          csA = 0.0;
-          csB = 0.0;
+          const float zv = kr <= i ? z[r] : kMasked;                // masked: weight exactly 0
+          wgt[r] = exp2_rel(zv, mr[u], c_hi, c_lo) * iz[u];
         }
       }
+      if (qp == 16) {                       // rows 0-7 of the lane are head 2 mb, rows 8-15 head 2 mb + 1
+        hsA += (double)pair_sum<8>(wgt);
+        hsB += (double)pair_sum<8>(wgt + 8);
+      } else {
+        hsA += (double)pair_sum<16>(wgt);
+      }
+      if (qp == 16 || (32 * (mb + 1)) % qp == 0) {     // the block ends a head (qp = 16: two)
+        const int jA = qp == 16 ? 2 * mb : (32 * mb) / qp;
+        const double a = hsA + __shfl_xor(hsA, 32, kWave);
+        if (hf == 0 && key < L && jA < G) s_h[(size_t)(g * G + jA) * L + key] = (float)a;
+        if (qp == 16) {
+          const double bsum = hsB + __shfl_xor(hsB, 32, kWave);
+          if (hf == 0 && key < L && jA + 1 < G) s_h[(size_t)(g * G + jA + 1) * L + key] = (float)bsum;
+        }
+        hsA = 0.0;
+        hsB = 0.0;
+      }
+      __builtin_amdgcn_sched_barrier(0);    // one row block at a time, as in pass 1
     }
   }
 }
@@ -432,10 +446,11 @@ static bool use_mfma(int dtype, int Hq, int Hkv, int q) {
 // dynamic LDS of the two kernels for Rp rows of head dimension D (pass 1 is the larger)
 static size_t score_mfma_smem(int Rp, int D) { return (size_t)Rp * D * 2 + (size_t)Rp * 4 * (8 + 4); }
 
-template <int D>
+template <int D, int MB>
 static hipError_t run_score_mfma(const void* Q, const void* K, int64_t L, int Hq, int Hkv, int q, float* s_h,
                                  double2* part, double2* rowstat, hipStream_t st) {
-  const int qp = score_qp(q), Rp = score_rows_padded(Hq, Hkv, q);
+  constexpr int Rp = 32 * MB;
+  const int qp = score_qp(q);
   const double scale = 1.0 / sqrt((double)D), c = scale * 1.4426950408889634;
   // keys per block: 1024 when that still gives ~2 blocks per CU, down to 256 for short sequences
   int nsub = 4;
@@ -445,25 +460,40 @@ static hipError_t run_score_mfma(const void* Q, const void* K, int64_t L, int Hq
   const uint16_t* Kt = static_cast<const uint16_t*>(K);
   const size_t smem = score_mfma_smem(Rp, D);
   if (smem > 48 * 1024) {                     // up to 76 KB for 256 rows: raise the dynamic-LDS limit
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_p1_kernel<D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_p1_kernel<D, MB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_p2_kernel<D>),
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&score_p2_kernel<D, MB>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  score_p1_kernel<D><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part);
+  score_p1_kernel<D, MB><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, part);
   const int64_t nrows = (int64_t)Hkv * Rp;
   score_combine_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(part, nrows, grid.x, scale, rowstat);
-  score_p2_kernel<D><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, rowstat, s_h);
+  score_p2_kernel<D, MB><<<grid, 256, smem, st>>>(Qt, Kt, L, Hq, Hkv, q, qp, nsub, c, rowstat, s_h);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t run_score_mfma_rows(const void* Q, const void* K, int64_t L, int Hq, int Hkv, int q, float* s_h,
+                                      double2* part, double2* rowstat, hipStream_t st) {
+  switch (score_rows_padded(Hq, Hkv, q) / 32) {
+    case 1: return run_score_mfma<D, 1>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    case 2: return run_score_mfma<D, 2>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    case 3: return run_score_mfma<D, 3>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    case 4: return run_score_mfma<D, 4>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    case 5: return run_score_mfma<D, 5>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    case 6: return run_score_mfma<D, 6>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    case 7: return run_score_mfma<D, 7>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    default: return run_score_mfma<D, 8>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+  }
 }
 
 hipError_t launch_score(int dtype, int d, const void* Q, const void* K, int64_t L, int Hq, int Hkv,
                         int q, float* s_h, double2* part, double2* rowstat, hipStream_t st) {
   if (use_mfma(dtype, Hq, Hkv, q))
-    return d == 128 ? run_score_mfma<128>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st)
-                    : run_score_mfma<64>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
+    return d == 128 ? run_score_mfma_rows<128>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st)
+                    : run_score_mfma_rows<64>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
   if (dtype == 1) {
     return d == 128 ? run_score<uint16_t, 128>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st)
                     : run_score<uint16_t, 64>(Q, K, L, Hq, Hkv, q, s_h, part, rowstat, st);
