@@ -22,7 +22,8 @@ sys.path.insert(0, ROOT)
 
 from token_sparse_attention_amd import binding  # noqa: E402
 from token_sparse_attention_amd.configs import WORKLOADS  # noqa: E402
-from token_sparse_attention_amd.inputs import make_batch, make_layer  # noqa: E402
+from token_sparse_attention_amd.inputs import chain_drift_values, iter_chain, make_batch, make_layer  # noqa: E402
+from token_sparse_attention_amd.runtime import select_sparse_layers  # noqa: E402
 
 METRIC = "TSA layer ms & speedup vs own dense attn at L=128K; MFMA util, HBM GB/s"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
@@ -273,6 +274,47 @@ def cpu_baseline(cfg, inp, k_gpu, Lp_gpu, Y_gpu, idx_gpu, pending=(), budget_s=1
     return base, par, sweeps
 
 
+class _QRows:
+    """Head h's compressed query rows Q[pos[i], h] read only where the oracle asks for them (its
+    attention takes the sampled rows of Q_hat); shape as the full [len(pos)][d] array."""
+
+    def __init__(self, Q, pos, h, d):
+        self.Q, self.pos, self.h, self.shape = Q, pos, h, (len(pos), d)
+
+    def __getitem__(self, rows):
+        return np.asarray(self.Q[self.pos[rows], self.h, :], dtype=np.float64)
+
+
+class _F64Rows:
+    """Indexing into a stored (bf16) host tensor that returns float64 numpy rows, so the verdict can
+    read a 256K layer's rows without widening the whole tensor."""
+
+    def __init__(self, t):
+        self.t = t
+
+    def __getitem__(self, key):
+        return self.t[key].double().numpy()
+
+
+def chain_verdicts(cfg, pending):
+    """The oracle leg for the 256K chain's lines (its tau sweep and its sparse layers): the oracle's
+    scores of each line's own layer inputs, then sweep_verdict on that line.  Part of the CPU-baseline
+    (oracle) leg: skipped with --no-cpu-baseline."""
+    import oracle
+    out, cache = [], {}
+    for _, ev in pending:
+        inp = ev["inputs"]
+        key = id(inp["K"])
+        if key not in cache:
+            cache.clear()
+            s_h = oracle.head_scores_recent(inp["Q"][cfg.L - cfg.q:].double().numpy(), inp["K"].double().numpy())
+            cache[key] = (s_h, oracle.layer_score(s_h))
+        s_h, s_l = cache[key]
+        out.append(sweep_verdict(cfg, _F64Rows(inp["Q"]), _F64Rows(inp["K"]), _F64Rows(inp["V"]), _F64Rows(ev["X_in"]),
+                                 s_h, s_l, ev))
+    return out
+
+
 def sweep_verdict(cfg, Q, K, V, X, s_h, s_l, ev):
     """One supplementary line against the oracle (float64 inputs Q, K, V, X and the oracle's s_h,
     s_l of the same workload), with the parity tests' rules: the keep count (the fixed-ratio count
@@ -314,7 +356,7 @@ def sweep_verdict(cfg, Q, K, V, X, s_h, s_l, ev):
         if h not in ok_heads:
             continue
         pos = sel[h]
-        Qh, Kh, Vh = Q[pos, h, :], K[pos, h // G, :], V[pos, h // G, :]
+        Qh, Kh, Vh = _QRows(Q, pos, h, cfg.d), K[pos, h // G, :], V[pos, h // G, :]
         if ev["kind"] == "block":
             keep = oracle.block_select(oracle.block_pool(Qh, Lp), oracle.block_pool(Kh, Lp), ev["gamma"])
             gl = ev["block_lists"][h]
@@ -795,6 +837,84 @@ def measure_workload(cfg, Q, K, V, X, steps, warmup, stream, sample_clocks=False
     return rec, {"Y": Y, "idx": idx, "k": k, "Lp": Lp, "clocks": clocks, "att_tf": att_tf, "peak": peak}
 
 
+CHAIN_PARITY_HEADS = (0, 13, 18, 31)
+
+
+def chain_c5(steps, warmup, stream, dev, with_evidence=True):
+    """The 8-layer attention-only chain at L = 256K (32/8 heads, d = 128, q = 64, tau = 0.002): the
+    least-drifting half (layers 5-8, from the seeded drift values) run Token Sparse Attention, the
+    others dense causal attention, and the residual X is carried from each layer to the next.  Each
+    layer's inputs are drawn from the chain recipe just before it runs and are resident in HBM when
+    it is timed.  For the speedup over an all-dense chain the dense attention is also timed on the
+    sparse layers' inputs.  Before the chain runs, the coverage thresholds of the pages' sparsity
+    regime are swept on layer 1's inputs at this shape.  Returns the chain record, the sweep lines
+    and, for the oracle leg, the evidence of every sparse line."""
+    cfg = WORKLOADS[5]
+    sparse = select_sparse_layers(chain_drift_values(cfg))
+    s = binding.shape_of(cfg)
+    ws = binding.workspace(binding.layer_workspace_bytes(s), dev)
+    dws = binding.workspace(binding.dense_workspace_bytes(s), dev)
+    kLp = torch.zeros(2, dtype=torch.int32, device=dev)
+    X = Y = Yd = None
+    layers, sweep, pend = [], [], []
+    t_start = time.perf_counter()
+    for layer_id, inp in iter_chain(cfg):
+        Q, K, V = (inp[n].to(dev) for n in ("Q", "K", "V"))
+        if X is None:
+            X = inp["X"].to(dev)
+            Y, Yd = torch.empty_like(X), torch.empty_like(X)
+        keep = {n: inp[n] for n in ("Q", "K", "V")} if with_evidence else None
+        del inp
+        if layer_id == 1:
+            X_in1 = X.cpu() if with_evidence else None
+            for tau in (0.15, 0.50, 0.72):
+                st = binding.shape(cfg.L, cfg.Hq, cfg.Hkv, cfg.d, cfg.q, tau, cfg.dtype)
+                tl, td = timed_pair(lambda: binding.layer(st, Q, K, V, X, Y, kLp, ws),
+                                    lambda: binding.dense_attn_causal(st, Q, K, V, X, Yd, dws), max(2, steps // 2), 1,
+                                    stream)
+                k, Lp = kLp.tolist()
+                line = {"tau": tau, "k": k, "L_keep": Lp, "pruned_frac": round(k / cfg.L, 4),
+                        "layer_ms": round(float(np.median(tl)), 3), "dense_ms": round(float(np.median(td)), 3),
+                        "speedup_vs_dense": round(float(np.median(td)) / float(np.median(tl)), 3)}
+                sweep.append(line)
+                if with_evidence:
+                    ev = sweep_evidence(cfg, st, Q, K, V, X, lambda Yn, kl: binding.layer(st, Q, K, V, X, Yn, kl, ws),
+                                        lambda: _stage_selection(cfg, st, Q, K, lambda sl, kl, w: binding.budget(
+                                            st, sl, kl[0:1], kl[1:2], w)), heads=CHAIN_PARITY_HEADS,
+                                        rows_per_head=6, seed=int(tau * 100))
+                    pend.append((line, dict(ev, kind="tau", tau=tau, inputs=keep, X_in=X_in1)))
+            progress("c5 tau sweep done")
+        rec = {"layer": layer_id, "kind": "sparse" if layer_id in sparse else "dense"}
+        if layer_id in sparse:
+            tl, td = timed_pair(lambda: binding.layer(s, Q, K, V, X, Y, kLp, ws),
+                                lambda: binding.dense_attn_causal(s, Q, K, V, X, Yd, dws), steps, warmup, stream)
+            k, Lp = kLp.tolist()
+            rec.update({"ms": round(float(np.median(tl)), 3), "ms_percentiles": pct(tl), "k": k, "L_keep": Lp,
+                        "dense_ms_same_inputs": round(float(np.median(td)), 3)})
+            if with_evidence:
+                X_in = X.cpu()
+                ev = sweep_evidence(cfg, s, Q, K, V, X, lambda Yn, kl: binding.layer(s, Q, K, V, X, Yn, kl, ws),
+                                    lambda: _stage_selection(cfg, s, Q, K, lambda sl, kl, w: binding.budget(
+                                        s, sl, kl[0:1], kl[1:2], w)), heads=CHAIN_PARITY_HEADS, rows_per_head=6,
+                                    seed=layer_id)
+                pend.append((rec, dict(ev, kind="tau", tau=cfg.tau, inputs=keep, X_in=X_in)))
+            binding.layer(s, Q, K, V, X, Y, kLp, ws)          # the chain's own pass: Y = this layer's output
+        else:
+            td = timed_calls(lambda: binding.dense_attn_causal(s, Q, K, V, X, Y, dws), steps, warmup, stream)
+            rec.update({"ms": round(float(np.median(td)), 3), "ms_percentiles": pct(td),
+                        "dense_ms_same_inputs": round(float(np.median(td)), 3)})
+        X, Y = Y, X                                            # the residual stream carried to the next layer
+        layers.append(rec)
+        progress(f"c5 chain layer {layer_id} ({rec['kind']}): {rec['ms']:.1f} ms")
+        del Q, K, V, keep
+    total = sum(r["ms"] for r in layers)
+    dense_total = sum(r["dense_ms_same_inputs"] for r in layers)
+    out = {"workload": cfg.name, "sparse_layers": sparse, "layers": layers, "total_ms": round(total, 3),
+           "all_dense_total_ms": round(dense_total, 3), "speedup_vs_all_dense": round(dense_total / total, 4),
+           "wall_s": round(time.perf_counter() - t_start, 1)}
+    return out, sweep, pend
+
+
 def graph_replay(steps, warmup, stream, dev):
     """The fused layer captured once in a HIP graph and replayed, against the same call made
     eagerly, on the shorter workloads (where ~21 small launches weigh most) and on the varlen batch.
@@ -856,6 +976,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay line")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the per-workload records of the other workloads")
+    ap.add_argument("--no-chain", action="store_true", help="skip the 8-layer 256K chain (and its tau sweep)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only run the short kernel sequence used for the rocprofv3 counter passes")
     ap.add_argument("--varlen-trace", action="store_true",
@@ -955,7 +1076,7 @@ def main():
     if not args.no_configs:
         recs = []
         for n in sorted(WORKLOADS):
-            if n == args.workload:
+            if n == args.workload or WORKLOADS[n].layers > 1:      # the chain has a record of its own
                 continue
             c = WORKLOADS[n]
             t0 = time.perf_counter()
@@ -969,6 +1090,21 @@ def main():
             del Qc, Kc, Vc, Xc, _
             torch.cuda.empty_cache()
         out["supplementary_configs"] = recs
+    if not args.no_chain and args.workload != 5:
+        evidence = not args.no_cpu_baseline
+        out["supplementary_chain_c5"], sweep5, pend5 = chain_c5(3, 1, stream, dev, with_evidence=evidence)
+        out["supplementary_tau_sweep_c5"] = sweep5
+        if evidence:
+            for (line, _), v in zip(pend5, chain_verdicts(WORKLOADS[5], pend5)):
+                line["parity_vs_oracle"] = v
+            progress(f"c5 chain and sweep judged: {sum(v['parity_vs_oracle']['pass'] for v, _ in pend5)} of "
+                     f"{len(pend5)} lines pass")
+        for line, _ in pend5:
+            if not line.get("parity_vs_oracle", {}).get("pass", False):
+                key = "speedup_vs_dense" if "speedup_vs_dense" in line else None
+                if key:
+                    line["speedup_vs_dense_withheld"] = line.pop(key)
+        del pend5
     print(json.dumps(out), flush=True)
 
 
