@@ -31,6 +31,8 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
+// bf16 attention weights exp2((s - m) * scale * log2 e) stay below 2^kLazyLog2 (lazy rescale)
+constexpr float kLazyLog2 = 8.0f;
 // waves (of 32 query rows each) per workgroup of the dense and compressed bf16 kernels: 8 (one
 // 512-thread workgroup per CU, still two waves per SIMD) so that every K/V tile brought into LDS
 // serves 256 query rows; the block-sparse variant keeps 4 (its key-block lists are per 128 rows).
@@ -355,12 +357,18 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[t][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    if (mx > m_run) {
-      const float alpha = __builtin_amdgcn_exp2f((m_run - mx) * sl2);
+    // Lazy rescale: a row's reference m_run (the exponent offset) moves only when the row maximum
+    // passes it by more than kLazyLog2 in the exponent, so the weights stay below 2^kLazyLog2.  When
+    // any row of the wave's 32 passes, every row moves to its own maximum (alpha is exactly 1 where
+    // it did not grow); the branch is wave-uniform and, past the first tiles, almost never taken.
+    const bool grow = (mx - m_run) * sl2 > kLazyLog2;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * sl2);
 #pragma unroll
       for (int t = 0; t < DT; ++t) o[t] *= alpha;
       l_run *= alpha;
-      m_run = mx;
+      m_run = mnew;
     }
     const float mb2 = m_run * sl2;
     // next tile's score MFMAs issued in program order with this tile's exponentials (EPC per MFMA),

@@ -6,9 +6,11 @@
 //   pass 1: logits for every recent query row of the group; per-wave (max, sum of exp) partials;
 //   combine: per row, the global max m and 1 / sum_t exp(z - m), float64, fixed order;
 //   pass 2: the same logits again; w = exp(z - m) / Z summed over each head's q rows -> s_h.
-// The dot products, exponentials and sums are float64: the score decides a discrete selection, so
-// it is kept far below the 1e-6 relative tie band of the selection (its only rounding is the final
-// store to float32).  Both passes compute bit-identical logits.
+// The score decides a discrete selection, so its error is kept far below the selection's 1e-6
+// relative tie band.  The vector-ALU kernel below (fp32 inputs, and bf16 groups of more than 256
+// padded rows) forms dot products, exponentials and sums in float64, its only rounding the final
+// store to float32; the matrix-core kernels further down keep within a few 1e-7 (described there).
+// Both passes compute bit-identical logits.
 #include "kern_common.h"
 #include "tsa_internal.h"
 
