@@ -110,14 +110,27 @@ def timed_pair(fa, fb, steps, warmup, stream):
     return ta, tb
 
 
+def make_flush(dev):
+    """A 512 MiB float32 buffer whose read evicts every input from the 256 MB last-level cache."""
+    return torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+
+
+def evict(flush):
+    """Reads the flush buffer (one reduction).  A read leaves the caches clean: writing the buffer
+    instead would leave 256 MB of dirty lines whose write-back then lands inside the next timed call
+    (on this part that halves the rate of a following 268 MB read, 5.2 -> 2.7 TB/s)."""
+    return flush.amax()
+
+
 def timed_cold(fn, steps, warmup, stream, flush):
-    """Per-call ms of fn() over `steps` calls, each after writing a 512 MiB scratch buffer so the
+    """Per-call ms of fn() over `steps` calls, each after reading a 512 MiB scratch buffer so the
     256 MB last-level cache holds none of fn's inputs; HIP events around each call."""
     for _ in range(warmup):
         fn()
     times = []
     for _ in range(steps):
-        flush.fill_(1)
+        evict(flush)
+        torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record(stream)
@@ -136,8 +149,8 @@ def pct(times):
 
 def hbm_practical(dev, steps=10):
     """What plain torch device operations reach on this GPU, as context for the stage fractions
-    (all against the 8 TB/s published peak): a write-only fill and a copy of a 2 GiB buffer, median
-    of `steps` calls each."""
+    (all against the 8 TB/s published peak): a write-only fill, a copy and a read-only reduction of a
+    2 GiB buffer, median of `steps` calls each."""
     n = 2 << 30
     a = torch.empty(n, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
@@ -147,12 +160,15 @@ def hbm_practical(dev, steps=10):
     stream = torch.cuda.current_stream()
     fill_ms = float(np.median(timed_calls(lambda: a.fill_(3), steps, 1, stream)))
     copy_ms = float(np.median(timed_calls(lambda: b.copy_(a), steps, 1, stream)))
-    del a, b
+    af = a.view(torch.float32)
+    read_ms = float(np.median(timed_calls(lambda: af.amax(), steps, 1, stream)))
+    del a, b, af
     torch.cuda.empty_cache()
-    fill, copy = n / (fill_ms * 1e-3) / 1e9, 2 * n / (copy_ms * 1e-3) / 1e9
+    fill, copy, read = n / (fill_ms * 1e-3) / 1e9, 2 * n / (copy_ms * 1e-3) / 1e9, n / (read_ms * 1e-3) / 1e9
     return {"write_only_fill_GB_s": round(fill, 1), "fill_frac": round(fill / HBM_PEAK_GBS, 4),
             "copy_GB_s": round(copy, 1), "copy_frac": round(copy / HBM_PEAK_GBS, 4),
-            "how": "torch fill_ and copy_ on 2 GiB device buffers, median of per-call HIP events"}
+            "read_only_GB_s": round(read, 1), "read_frac": round(read / HBM_PEAK_GBS, 4),
+            "how": "torch fill_, copy_ and amax on 2 GiB device buffers, median of per-call HIP events"}
 
 
 def timed_calls(fn, steps, warmup, stream):
@@ -497,7 +513,7 @@ def traffic_probe(cfg, dev):
     """A short run for the counter passes: three compressed-attention launches on this workload's
     shape (L' = L, random bf16) and three copies of a 1 GiB buffer (the calibration of known size),
     then each memory-bound stage once through its own ABI call on this workload's inputs, after a
-    512 MiB write that evicts its inputs from the caches."""
+    512 MiB read that evicts its inputs from the caches."""
     s = binding.shape_of(cfg)
     C = binding.capacity(cfg.L)
     g = torch.Generator(device=dev).manual_seed(0)
@@ -525,14 +541,14 @@ def traffic_probe(cfg, dev):
     inv = torch.empty_like(idx)
     Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
     Y = torch.empty_like(X)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = make_flush(dev)
     stages = [("score", lambda: binding.score(s, Q, K, s_h, s_l, sws)),
               ("budget", lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws)),
               ("select", lambda: binding.select(s, s_h, kl[1:2], idx, inv, sws)),
               ("gather", lambda: binding.gather(s, Q, K, V, idx, kl[1:2], Qh, Kh, Vht)),
               ("scatter", lambda: binding.scatter_residual(s, Oh, idx, inv, kl[1:2], X, Y))]
     for _, fn in stages:
-        flush.fill_(1)
+        evict(flush)
         fn()
         torch.cuda.synchronize()
     print(json.dumps({"traffic_probe": cfg.name, "copy_bytes": 1 << 30, "attention_launches": 3,
@@ -791,7 +807,7 @@ def measure_workload(cfg, Q, K, V, X, steps, warmup, stream, sample_clocks=False
     Vht = torch.empty(cfg.Hq, cfg.d, C, dtype=Q.dtype, device=dev)
     Oh = torch.empty_like(Qh)
     Ys = torch.empty_like(X)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = make_flush(dev)
     calls = {}
     calls["score"] = timed_cold(lambda: binding.score(s, Q, K, s_h, s_l, sws), steps, 1, stream, flush)
     calls["budget"] = timed_cold(lambda: binding.budget(s, s_l, kl[0:1], kl[1:2], sws), steps, 1, stream, flush)

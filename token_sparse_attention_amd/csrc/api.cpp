@@ -246,13 +246,13 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   // bf16 without block sparsity: the attention reads the query and key rows through idx and writes Y
   // itself (the gather of Q and K and the decompression folded into it; only V_hat^T is gathered);
   // the result is bitwise the same as gather -> attention -> scatter
+  // (fused: the rows no head kept are written by the gather's launch too)
   const bool fused = fused_layer(s, block_sparse);
   if (e == hipSuccess)
     e = launch_gather(s->dtype, s->d, Q, K, V, idx, kLp + 1, s->L, s->Hq, s->Hkv, C,
                       fused ? nullptr : at<void>(ws, w.Qh), fused ? nullptr : at<void>(ws, w.Kh), at<void>(ws, w.Vht),
-                      st);
+                      st, fused ? inv : nullptr, fused ? X : nullptr, fused ? Y : nullptr);
   if (fused) {
-    if (e == hipSuccess) e = launch_fill_unselected(s->dtype, s->d, inv, X, Y, s->L, s->Hq, st);
     if (e == hipSuccess) {
       const AttnSeqDesc one{0, 0, s->L, C, kLp + 1, idx};
       e = launch_attention_varlen(s->dtype, s->d, false, Q, K, at<void>(ws, w.Vht), 1, &one, s->Hq, s->Hkv, X, Y, st,
@@ -546,10 +546,8 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
     if (e == hipSuccess)
       e = launch_gather(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), tok(V, Hkv, b), idx, kl + 1, Lb, s->Hq,
                         s->Hkv, Cb, fused ? nullptr : comp(w.Qh, b), fused ? nullptr : comp(w.Kh, b), comp(w.Vht, b),
-                        st);
-    if (fused && e == hipSuccess)
-      e = launch_fill_unselected(s->dtype, s->d, inv, X ? tok(X, Hq, b) : nullptr,
-                                 static_cast<char*>(Y) + (size_t)cu_seqlens[b] * Hq * d * eb, Lb, s->Hq, st);
+                        st, fused ? inv : nullptr, fused && X ? tok(X, Hq, b) : nullptr,
+                        fused ? static_cast<char*>(Y) + (size_t)cu_seqlens[b] * Hq * d * eb : nullptr);
   }
   // stage 4b: one launch over every sample's ragged L'_b (fused: stage 5 in its epilogue)
   if (e == hipSuccess) {

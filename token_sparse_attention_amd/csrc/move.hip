@@ -58,27 +58,69 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
   }
 }
 
+// 16-byte LDS vectors of the bf16 gather's transpose tile: [d columns][128 rows / 8] (d = 128) or
+// [d][256 / 8] (d = 64)
+template <int D>
+constexpr int gather_lds_vectors() { return D * (256 / (D / 8)); }
+
+// The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
+// A block takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
+// coalesced load into LDS, and a block whose tokens are all selected stops there.  Then VPR
+// consecutive lanes move one 16-byte chunk each of a row, so every store instruction writes whole
+// rows: whole cache lines, which the streaming hint needs.  Rows written one 16-byte chunk per
+// instruction lose the L2's merging, which cost 3.3 ms on a 131072-token layer keeping a quarter of
+// its tokens.  Measured at L = 131072 (32 heads): a layer keeping nearly every row took 75.6 us when
+// every lane read its row's inverse-map entry itself.
+template <typename T, int D>
+__device__ __forceinline__ void fill_unselected_block(const int32_t* __restrict__ inv, const T* __restrict__ X,
+                                                      T* __restrict__ Y, int64_t L, int Hq, int h, int64_t bx,
+                                                      int32_t* sinv) {   // LDS, 260 entries
+  constexpr int VPR = D * (int)sizeof(T) / 16;
+  constexpr int TPB = 256 / VPR;                  // rows per pass; VPR passes cover the 256 tokens
+  const int c = threadIdx.x % VPR;
+  const int64_t base = bx * 256;
+  const int64_t tt = base + threadIdx.x;
+  const int32_t mine = tt < L ? inv[(size_t)h * L + tt] : 0;
+  sinv[threadIdx.x] = mine;
+  if ((threadIdx.x & 63) == 0) sinv[256 + threadIdx.x / 64] = 0;
+  const bool wave_any = __builtin_amdgcn_ballot_w64(mine < 0) != 0;
+  if (wave_any && (threadIdx.x & 63) == 0) sinv[256 + threadIdx.x / 64] = 1;
+  __syncthreads();
+  if ((sinv[256] | sinv[257] | sinv[258] | sinv[259]) == 0) return;   // every token of the block is selected
+  const uint4* X4 = reinterpret_cast<const uint4*>(X);
+#pragma unroll
+  for (int p = 0; p < VPR; ++p) {
+    const int r = p * TPB + (int)threadIdx.x / VPR;
+    const int64_t t = base + r;
+    if (t >= L || sinv[r] >= 0) continue;
+    const size_t e = ((size_t)t * Hq + h) * VPR + c;
+    st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), reinterpret_cast<uint4*>(Y) + e);
+  }
+}
+
+
 // bf16: a thread owns one 16-byte chunk (8 columns) of 8 consecutive compressed rows.  It loads that
 // chunk of the 8 gathered rows (16 threads cover a 256-byte row, so the loads stay coalesced) and
 // transposes the 8 x 8 block of 16-bit values in registers with byte permutes.  The resulting
 // 16-byte pieces (8 rows of one column) are regrouped through LDS, [column][row] with a XOR swizzle
 // of the piece slot, so that each column's run of TR rows leaves as contiguous 16-byte stores.
 template <int D>
-__global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                          const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
-                                                          const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
-                                                          int64_t C, uint16_t* __restrict__ Qh, uint16_t* __restrict__ Kh,
-                                                          uint16_t* __restrict__ Vht) {
+__device__ __forceinline__ void gather_bf16_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                  const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
+                                                  const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
+                                                  int64_t C, uint16_t* __restrict__ Qh, uint16_t* __restrict__ Kh,
+                                                  uint16_t* __restrict__ Vht, unsigned bid,
+                                                  uint4* tile) {        // LDS, gather_lds_vectors<D>()
   constexpr int VPR = D / 8;            // 16-byte chunks per row
   constexpr int NG = 256 / VPR;         // groups of 8 rows per block
   constexpr int TR = NG * 8;            // rows per block (128 for d = 128, 256 for d = 64)
   constexpr int PPC = TR / 8;           // 16-byte pieces per column in the block (= NG)
-  __shared__ uint4 tile[D * PPC];       // [column][piece], piece slot swizzled
+  // tile: [column][piece], piece slot swizzled
   // block -> (KV group, row tile, head of the group): the G heads of one (group, tile) pair are
-  // consecutive blocks of one XCD (blockIdx % 8), so its L2 serves the K/V rows they share
+  // consecutive blocks of one XCD (block index % 8), so its L2 serves the K/V rows they share
   const int G = Hq / Hkv;
   const int64_t ntiles = (L + TR - 1) / TR;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int xcd = bid & 7, slot = bid >> 3;
   const int64_t pair = (int64_t)(slot / G) * 8 + xcd;
   if (pair >= ntiles * Hkv) return;
   const int g = (int)(pair % Hkv), h = g * G + slot % G;
@@ -131,6 +173,36 @@ __global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __rest
     const int col = e / PPC, q = e % PPC;
     if ((int64_t)q * 8 >= nrows) continue;
     st_stream(tile[col * PPC + (q ^ (col % PPC))], reinterpret_cast<uint4*>(Vht + ((size_t)h * D + col) * C + b0 + 8 * q));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void gather_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                          const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
+                                                          int64_t C, uint16_t* __restrict__ Qh, uint16_t* __restrict__ Kh,
+                                                          uint16_t* __restrict__ Vht) {
+  __shared__ uint4 tile[gather_lds_vectors<D>()];
+  gather_bf16_block<D>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, blockIdx.x, tile);
+}
+
+// The fused layer's gather with its unselected-row fill in the same launch: blocks [0, ngather)
+// gather, the Hq * ceil(L / 256) blocks after them fill (the two touch disjoint memory).
+template <int D>
+__global__ __launch_bounds__(256) void gather_fill_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                               const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
+                                                               const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
+                                                               int64_t C, uint16_t* __restrict__ Qh, uint16_t* __restrict__ Kh,
+                                                               uint16_t* __restrict__ Vht, unsigned ngather,
+                                                               const int32_t* __restrict__ inv, const uint16_t* __restrict__ X,
+                                                               uint16_t* __restrict__ Y) {
+  __shared__ uint4 lds[gather_lds_vectors<D>()];   // one role per block: the fill reuses it
+  if (blockIdx.x < ngather) {
+    gather_bf16_block<D>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, blockIdx.x, lds);
+  } else {
+    const int64_t f = blockIdx.x - ngather, per_head = (L + 255) / 256;
+    fill_unselected_block<uint16_t, D>(inv, X, Y, L, Hq, (int)(f / per_head), f % per_head,
+                                       reinterpret_cast<int32_t*>(lds));
   }
 }
 
@@ -208,53 +280,7 @@ __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ 
   }
 }
 
-// The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
-// A block takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
-// coalesced load into LDS, and a block whose tokens are all selected stops there.  Then VPR
-// consecutive lanes move one 16-byte chunk each of a row, so every store instruction writes whole
-// rows: whole cache lines, which the streaming hint needs.  Rows written one 16-byte chunk per
-// instruction lose the L2's merging, which cost 3.3 ms on a 131072-token layer keeping a quarter of
-// its tokens.  Measured at L = 131072 (32 heads): a layer keeping nearly every row took 75.6 us when
-// every lane read its row's inverse-map entry itself.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fill_unselected_kernel(const int32_t* __restrict__ inv, const T* __restrict__ X,
-                                                              T* __restrict__ Y, int64_t L, int Hq) {
-  constexpr int VPR = D * (int)sizeof(T) / 16;
-  constexpr int TPB = 256 / VPR;                  // rows per pass; VPR passes cover the 256 tokens
-  __shared__ int32_t sinv[256];
-  const int h = blockIdx.y, c = threadIdx.x % VPR;
-  const int64_t base = (int64_t)blockIdx.x * 256;
-  const int64_t tt = base + threadIdx.x;
-  const int32_t mine = tt < L ? inv[(size_t)h * L + tt] : 0;
-  sinv[threadIdx.x] = mine;
-  if (!__syncthreads_or(mine < 0)) return;        // every token of the block is selected
-  const uint4* X4 = reinterpret_cast<const uint4*>(X);
-#pragma unroll
-  for (int p = 0; p < VPR; ++p) {
-    const int r = p * TPB + (int)threadIdx.x / VPR;
-    const int64_t t = base + r;
-    if (t >= L || sinv[r] >= 0) continue;
-    const size_t e = ((size_t)t * Hq + h) * VPR + c;
-    st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), reinterpret_cast<uint4*>(Y) + e);
-  }
-}
 
-template <typename T, int D>
-static hipError_t run_fill_unselected(const int32_t* inv, const void* X, void* Y, int64_t L, int Hq, hipStream_t st) {
-  const dim3 grid((unsigned)((L + 255) / 256), (unsigned)Hq);
-  fill_unselected_kernel<T, D><<<grid, 256, 0, st>>>(inv, static_cast<const T*>(X), static_cast<T*>(Y), L, Hq);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_unselected(int dtype, int d, const int32_t* inv, const void* X, void* Y, int64_t L, int Hq,
-                                  hipStream_t st) {
-  if (X == Y) return hipSuccess;             // in place: those rows already hold X
-  if (dtype == 1)
-    return d == 128 ? run_fill_unselected<uint16_t, 128>(inv, X, Y, L, Hq, st)
-                    : run_fill_unselected<uint16_t, 64>(inv, X, Y, L, Hq, st);
-  return d == 128 ? run_fill_unselected<float, 128>(inv, X, Y, L, Hq, st)
-                  : run_fill_unselected<float, 64>(inv, X, Y, L, Hq, st);
-}
 
 // Index-driven variant (no inverse map): Y must already hold X (or zeros for a pure decompress).
 template <typename T, int D>
@@ -291,16 +317,25 @@ static unsigned grid_for(size_t n) {
 template <typename T, int D>
 static hipError_t run_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                              const int32_t* Lp_dev, int64_t L, int Hq, int Hkv, int64_t C, void* Qh,
-                             void* Kh, void* Vht, hipStream_t st) {
+                             void* Kh, void* Vht, hipStream_t st, const int32_t* inv, const void* X, void* Y) {
   if constexpr (sizeof(T) == 2) {
     constexpr int TR = 256 / (D / 8) * 8;
     const int64_t pairs = (L + TR - 1) / TR * Hkv;
     const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
-    gather_bf16_kernel<D><<<nblk, 256, 0, st>>>(static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-                                                static_cast<const uint16_t*>(V), idx, Lp_dev, L, Hq, Hkv, C,
-                                                static_cast<uint16_t*>(Qh), static_cast<uint16_t*>(Kh),
-                                                static_cast<uint16_t*>(Vht));
+    const auto Qt = static_cast<const uint16_t*>(Q), Kt = static_cast<const uint16_t*>(K);
+    const auto Vt = static_cast<const uint16_t*>(V);
+    if (Y) {
+      const unsigned nfill = (unsigned)((L + 255) / 256 * Hq);
+      gather_fill_bf16_kernel<D><<<nblk + nfill, 256, 0, st>>>(Qt, Kt, Vt, idx, Lp_dev, L, Hq, Hkv, C,
+                                                               static_cast<uint16_t*>(Qh), static_cast<uint16_t*>(Kh),
+                                                               static_cast<uint16_t*>(Vht), nblk, inv,
+                                                               static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y));
+    } else {
+      gather_bf16_kernel<D><<<nblk, 256, 0, st>>>(Qt, Kt, Vt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Qh),
+                                                  static_cast<uint16_t*>(Kh), static_cast<uint16_t*>(Vht));
+    }
   } else {
+    if (Y) return hipErrorInvalidValue;   // the fused fill is bf16 only
     const dim3 grid((unsigned)((L + kTileRows - 1) / kTileRows), (unsigned)Hq);
     gather_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(Q), static_cast<const T*>(K),
                                               static_cast<const T*>(V), idx, Lp_dev, L, Hq, Hkv, C,
@@ -311,12 +346,14 @@ static hipError_t run_gather(const void* Q, const void* K, const void* V, const 
 
 hipError_t launch_gather(int dtype, int d, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
-                         int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st) {
+                         int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st, const int32_t* inv,
+                         const void* X, void* Y) {
+  if (Y && X == Y) Y = nullptr;          // in place: the unselected rows already hold X
   if (dtype == 1)
-    return d == 128 ? run_gather<uint16_t, 128>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st)
-                    : run_gather<uint16_t, 64>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st);
-  return d == 128 ? run_gather<float, 128>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st)
-                  : run_gather<float, 64>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st);
+    return d == 128 ? run_gather<uint16_t, 128>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st, inv, X, Y)
+                    : run_gather<uint16_t, 64>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st, inv, X, Y);
+  return d == 128 ? run_gather<float, 128>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st, inv, X, Y)
+                  : run_gather<float, 64>(Q, K, V, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, Vht, st, inv, X, Y);
 }
 
 template <typename T, int D>

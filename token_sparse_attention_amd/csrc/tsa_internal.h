@@ -58,15 +58,15 @@ hipError_t launch_select(const float* s_h, int64_t L, int Hq, const int32_t* Lp_
                          int32_t* idx, int32_t* inv, hipStream_t st);
 
 // ---- move.hip -----------------------------------------------------------------------------------
+// With Y (bf16 only), the same launch also writes the rows outside every selection:
+// Y[t][h] = X[t][h] (or +0.0 without X) where inv[h][t] < 0, nothing when Y aliases X.  (The fused
+// layer writes the selected rows from the attention epilogue.)
 hipError_t launch_gather(int dtype, int d, const void* Q, const void* K, const void* V,
                          const int32_t* idx, const int32_t* Lp_dev, int64_t L, int Hq, int Hkv,
-                         int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st);
+                         int64_t C, void* Qh, void* Kh, void* Vht, hipStream_t st, const int32_t* inv = nullptr,
+                         const void* X = nullptr, void* Y = nullptr);
 hipError_t launch_transpose_v(int dtype, int d, const void* V, int64_t L, int Hkv, int64_t C,
                               void* Vt, hipStream_t st);
-// Rows outside every selection: Y[t][h] = X[t][h] (or +0.0 without X) where inv[h][t] < 0; nothing
-// when Y aliases X.  (The fused layer writes the selected rows from the attention epilogue.)
-hipError_t launch_fill_unselected(int dtype, int d, const int32_t* inv, const void* X, void* Y, int64_t L, int Hq,
-                                  hipStream_t st);
 hipError_t launch_scatter(int dtype, int d, const void* Oh, const int32_t* idx, const int32_t* inv,
                           const int32_t* Lp_dev, const void* X, void* Y, int64_t L, int Hq,
                           int64_t C, hipStream_t st);
