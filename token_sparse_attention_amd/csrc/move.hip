@@ -59,14 +59,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
   }
 }
 
-// Row groups of 8 per thread in the bf16 V^T gather (128 rows per block at d = 128).  Two groups
-// (256 rows, each column's run leaving as one 512-byte store, 64 KB of LDS) measured 12% slower at
-// L = 131072 than one: the LDS then allows only 2 workgroups per CU instead of 5.
-constexpr int kVtGpt = 1;
-
-// 16-byte LDS vectors of the bf16 V^T gather's transpose tile: [d columns][rows / 8]
-template <int D, int GPT>
-constexpr int gather_lds_vectors() { return D * (256 / (D / 8)) * GPT; }
+// 16-byte LDS vectors of the bf16 V^T gather's transpose tile for NT threads: [d columns][rows / 8],
+// rows = 8 NT / (d / 8).  Two row groups per thread (256 rows, each column's run leaving as one
+// 512-byte store, 64 KB of LDS) measured 12% slower at L = 131072 than one: the LDS then allows only
+// 2 workgroups per CU instead of 5.
+template <int D, int NT>
+constexpr int gather_lds_vectors() { return D * (NT / (D / 8)); }
 
 // The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
 // A block takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
@@ -109,15 +107,15 @@ __device__ __forceinline__ void fill_unselected_block(const int32_t* __restrict_
 // transposes the 8 x 8 block of 16-bit values in registers with byte permutes.  The resulting
 // 16-byte pieces (8 rows of one column) are regrouped through LDS, [column][row] with a XOR swizzle
 // of the piece slot, so that each column's run of TR rows leaves as contiguous 16-byte stores.
-template <int D, int GPT>
+template <int D, int NT>
 __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
                                                      int64_t C, uint16_t* __restrict__ Vht, unsigned bid,
-                                                     uint4* tile) {     // LDS, gather_lds_vectors<D, GPT>()
+                                                     uint4* tile) {     // LDS, gather_lds_vectors<D, NT>()
   constexpr int VPR = D / 8;            // 16-byte chunks per row
-  constexpr int NG = 256 / VPR;         // groups of 8 rows per pass of the block's threads
-  constexpr int TR = NG * 8 * GPT;      // rows per block (GPT groups per thread)
-  constexpr int PPC = TR / 8;           // 16-byte pieces per column in the block
+  constexpr int NG = NT / VPR;          // groups of 8 rows per block
+  constexpr int TR = NG * 8;            // rows per block
+  constexpr int PPC = TR / 8;           // 16-byte pieces per column in the block (= NG)
   // tile: [column][piece], piece slot swizzled
   // block -> (KV group, row tile, head of the group): the G heads of one (group, tile) pair are
   // consecutive blocks of one XCD (block index % 8), so its L2 serves the V rows they share
@@ -130,58 +128,56 @@ __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict_
   const int64_t Lp = Lp_dev[0];
   const int64_t b0 = (pair / Hkv) * TR;
   if (b0 >= Lp) return;
-  const int c = threadIdx.x % VPR;
+  const int c = threadIdx.x % VPR, grp = threadIdx.x / VPR;
+  const int64_t r0 = b0 + grp * 8;
   const uint4* V4 = reinterpret_cast<const uint4*>(V);
-  uint32_t v[GPT][8][4];
+  uint32_t v[8][4];
 #pragma unroll
-  for (int gi = 0; gi < GPT; ++gi) {
-    const int64_t r0 = b0 + (gi * NG + threadIdx.x / VPR) * 8;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t i = r0 + u;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (i < Lp) x = V4[((size_t)idx[(size_t)h * L + i] * Hkv + g) * VPR + c];
-      v[gi][u][0] = x.x; v[gi][u][1] = x.y; v[gi][u][2] = x.z; v[gi][u][3] = x.w;
-    }
+  for (int u = 0; u < 8; ++u) {
+    const int64_t i = r0 + u;
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (i < Lp) x = V4[((size_t)idx[(size_t)h * L + i] * Hkv + g) * VPR + c];
+    v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
   }
   // column 2j of the chunk is the low half of word j of every row, column 2j+1 the high half; word
   // m of a column piece pairs rows 2m (low) and 2m+1 (high).  Piece grp of column col sits in slot
   // grp ^ (col % PPC) of that column's LDS row.
 #pragma unroll
-  for (int gi = 0; gi < GPT; ++gi) {
-    const int grp = gi * NG + threadIdx.x / VPR;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 lo, hi;
-      lo.x = __builtin_amdgcn_perm(v[gi][1][j], v[gi][0][j], 0x05040100u);
-      lo.y = __builtin_amdgcn_perm(v[gi][3][j], v[gi][2][j], 0x05040100u);
-      lo.z = __builtin_amdgcn_perm(v[gi][5][j], v[gi][4][j], 0x05040100u);
-      lo.w = __builtin_amdgcn_perm(v[gi][7][j], v[gi][6][j], 0x05040100u);
-      hi.x = __builtin_amdgcn_perm(v[gi][1][j], v[gi][0][j], 0x07060302u);
-      hi.y = __builtin_amdgcn_perm(v[gi][3][j], v[gi][2][j], 0x07060302u);
-      hi.z = __builtin_amdgcn_perm(v[gi][5][j], v[gi][4][j], 0x07060302u);
-      hi.w = __builtin_amdgcn_perm(v[gi][7][j], v[gi][6][j], 0x07060302u);
-      const int col = 8 * c + 2 * j;
-      tile[col * PPC + (grp ^ (col % PPC))] = lo;
-      tile[(col + 1) * PPC + (grp ^ ((col + 1) % PPC))] = hi;
-    }
+  for (int j = 0; j < 4; ++j) {
+    uint4 lo, hi;
+    lo.x = __builtin_amdgcn_perm(v[1][j], v[0][j], 0x05040100u);
+    lo.y = __builtin_amdgcn_perm(v[3][j], v[2][j], 0x05040100u);
+    lo.z = __builtin_amdgcn_perm(v[5][j], v[4][j], 0x05040100u);
+    lo.w = __builtin_amdgcn_perm(v[7][j], v[6][j], 0x05040100u);
+    hi.x = __builtin_amdgcn_perm(v[1][j], v[0][j], 0x07060302u);
+    hi.y = __builtin_amdgcn_perm(v[3][j], v[2][j], 0x07060302u);
+    hi.z = __builtin_amdgcn_perm(v[5][j], v[4][j], 0x07060302u);
+    hi.w = __builtin_amdgcn_perm(v[7][j], v[6][j], 0x07060302u);
+    const int col = 8 * c + 2 * j;
+    tile[col * PPC + (grp ^ (col % PPC))] = lo;
+    tile[(col + 1) * PPC + (grp ^ ((col + 1) % PPC))] = hi;
   }
   __syncthreads();
   // each column's TR rows: PPC consecutive lanes store its PPC pieces contiguously
   const int64_t nrows = Lp - b0 < TR ? Lp - b0 : TR;
-  for (int e = threadIdx.x; e < D * PPC; e += 256) {
+  for (int e = threadIdx.x; e < D * PPC; e += NT) {
     const int col = e / PPC, q = e % PPC;
     if ((int64_t)q * 8 >= nrows) continue;
     st_stream(tile[col * PPC + (q ^ (col % PPC))], reinterpret_cast<uint4*>(Vht + ((size_t)h * D + col) * C + b0 + 8 * q));
   }
 }
 
+// Threads of the stage call's V^T gather: 256 (128 rows per block at d = 128).  128 threads (64
+// rows, 16 KB of LDS) measured 1.5% faster at L = 131072 but 2-4% slower at 32768, 64 threads 15%
+// slower at both.
+constexpr int kVtThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(256) void gather_vt_bf16_kernel(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(kVtThreads) void gather_vt_bf16_kernel(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
                                                              const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
                                                              int64_t C, uint16_t* __restrict__ Vht) {
-  __shared__ uint4 tile[gather_lds_vectors<D, kVtGpt>()];
-  gather_vt_bf16_block<D, kVtGpt>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, tile);
+  __shared__ uint4 tile[gather_lds_vectors<D, kVtThreads>()];
+  gather_vt_bf16_block<D, kVtThreads>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, tile);
 }
 
 // The fused layer's V^T gather with its unselected-row fill in the same launch: blocks [0, ngather)
@@ -193,9 +189,9 @@ __global__ __launch_bounds__(256) void gather_vt_fill_bf16_kernel(const uint16_t
                                                                   int Hkv, int64_t C, uint16_t* __restrict__ Vht,
                                                                   unsigned ngather, const int32_t* __restrict__ inv,
                                                                   const uint16_t* __restrict__ X, uint16_t* __restrict__ Y) {
-  __shared__ uint4 lds[gather_lds_vectors<D, kVtGpt>()];   // one role per block: the fill reuses it
+  __shared__ uint4 lds[gather_lds_vectors<D, 256>()];   // one role per block: the fill reuses it
   if (blockIdx.x < ngather) {
-    gather_vt_bf16_block<D, kVtGpt>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, lds);
+    gather_vt_bf16_block<D, 256>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, lds);
   } else {
     const int64_t f = blockIdx.x - ngather, per_head = (L + 255) / 256;
     fill_unselected_block<uint16_t, D>(inv, X, Y, L, Hq, (int)(f / per_head), f % per_head,
@@ -205,16 +201,18 @@ __global__ __launch_bounds__(256) void gather_vt_fill_bf16_kernel(const uint16_t
 
 // Row copies of the bf16 gather: Qh[h][i] = Q[idx[h][i]][h] and Kh[h][i] = K[idx[h][i]][g] for
 // rows i < L'.  VPR consecutive lanes move one row, 16 bytes each, so a wave's load covers whole
-// rows; a thread takes RPT rows and issues all their loads before its stores.  No LDS, so many more
-// waves stay resident than in the transposing kernel.  Block -> (KV group, row tile, head) as there,
-// so that one XCD's L2 serves the K rows the group's heads share.
+// rows; a thread moves one chunk of Q and one of K.  No LDS, so 8 waves per SIMD stay resident.  One
+// row per thread measured fastest at L = 131072 and 32768 (0.966 / 0.257 ms for the stage, against
+// 0.988 / 0.263 with 2 rows, 1.025 / 0.287 with 4 and 1.061 / 0.306 with 8, all loads issued before
+// the stores).  Block -> (KV group, row tile, head) as in the transposing kernel, so that one XCD's
+// L2 serves the K rows the group's heads share.
 template <int D>
 __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                                const int32_t* __restrict__ idx,
                                                                const int32_t* __restrict__ Lp_dev, int64_t L, int Hq,
                                                                int Hkv, int64_t C, uint16_t* __restrict__ Qh,
                                                                uint16_t* __restrict__ Kh) {
-  constexpr int VPR = D / 8, RPP = 256 / VPR, RPT = 4, TRC = RPP * RPT;
+  constexpr int VPR = D / 8, TRC = 256 / VPR;   // rows per block
   const int G = Hq / Hkv;
   const int64_t ntiles = (L + TRC - 1) / TRC;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -222,33 +220,16 @@ __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const uint16_t* _
   if (pair >= ntiles * Hkv) return;
   const int g = (int)(pair % Hkv), h = g * G + slot % G;
   const int64_t Lp = Lp_dev[0];
-  const int64_t b0 = (pair / Hkv) * TRC;
-  if (b0 >= Lp) return;
-  const int c = threadIdx.x % VPR, r = threadIdx.x / VPR;
-  const uint4* Q4 = reinterpret_cast<const uint4*>(Q);
-  const uint4* K4 = reinterpret_cast<const uint4*>(K);
-  uint4* Qh4 = reinterpret_cast<uint4*>(Qh);
-  uint4* Kh4 = reinterpret_cast<uint4*>(Kh);
-  int64_t t[RPT];
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    const int64_t i = b0 + u * RPP + r;
-    t[u] = i < Lp ? (int64_t)idx[(size_t)h * L + i] : -1;
-  }
-  uint4 qv[RPT], kv[RPT];
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    if (t[u] < 0) continue;
-    if (Qh4) qv[u] = ld_stream(&Q4[((size_t)t[u] * Hq + h) * VPR + c]);
-    if (Kh4) kv[u] = K4[((size_t)t[u] * Hkv + g) * VPR + c];
-  }
-#pragma unroll
-  for (int u = 0; u < RPT; ++u) {
-    if (t[u] < 0) continue;
-    const size_t dst = ((size_t)h * C + b0 + u * RPP + r) * VPR + c;
-    if (Qh4) st_stream(qv[u], &Qh4[dst]);
-    if (Kh4) st_stream(kv[u], &Kh4[dst]);
-  }
+  const int64_t i = (pair / Hkv) * TRC + threadIdx.x / VPR;
+  if (i >= Lp) return;
+  const int c = threadIdx.x % VPR;
+  const size_t t = (size_t)idx[(size_t)h * L + i];
+  const size_t dst = ((size_t)h * C + i) * VPR + c;
+  uint4 qv, kv;
+  if (Qh) qv = ld_stream(reinterpret_cast<const uint4*>(Q) + (t * Hq + h) * VPR + c);
+  if (Kh) kv = reinterpret_cast<const uint4*>(K)[(t * Hkv + g) * VPR + c];
+  if (Qh) st_stream(qv, reinterpret_cast<uint4*>(Qh) + dst);
+  if (Kh) st_stream(kv, reinterpret_cast<uint4*>(Kh) + dst);
 }
 
 // V [L][Hkv][d] -> Vt [Hkv][d][C], columns L .. C-1 zero (the dense path's value layout).
@@ -368,22 +349,25 @@ static hipError_t run_gather(const void* Q, const void* K, const void* V, const 
     const auto Vt = static_cast<const uint16_t*>(V);
     // the row copies of Q_hat and K_hat (no LDS, many waves), then the transposing V^T gather
     if (Qh || Kh) {
-      constexpr int TRC = 256 / (D / 8) * 4;
+      constexpr int TRC = 256 / (D / 8);
       const int64_t rpairs = (L + TRC - 1) / TRC * Hkv;
       const unsigned nrow = (unsigned)((rpairs + 7) / 8 * 8 * (Hq / Hkv));
       gather_rows_bf16_kernel<D><<<nrow, 256, 0, st>>>(Qt, Kt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Qh),
                                                        static_cast<uint16_t*>(Kh));
     }
-    constexpr int TR = 256 / (D / 8) * 8 * kVtGpt;
-    const int64_t pairs = (L + TR - 1) / TR * Hkv;
-    const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
     if (Y) {
+      constexpr int TR = 256 / (D / 8) * 8;
+      const int64_t pairs = (L + TR - 1) / TR * Hkv;
+      const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
       const unsigned nfill = (unsigned)((L + 255) / 256 * Hq);
       gather_vt_fill_bf16_kernel<D><<<nblk + nfill, 256, 0, st>>>(Vt, idx, Lp_dev, L, Hq, Hkv, C,
                                                                   static_cast<uint16_t*>(Vht), nblk, inv,
                                                                   static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y));
     } else {
-      gather_vt_bf16_kernel<D><<<nblk, 256, 0, st>>>(Vt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Vht));
+      constexpr int TR = kVtThreads / (D / 8) * 8;
+      const int64_t pairs = (L + TR - 1) / TR * Hkv;
+      const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
+      gather_vt_bf16_kernel<D><<<nblk, kVtThreads, 0, st>>>(Vt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Vht));
     }
   } else {
     if (Y) return hipErrorInvalidValue;   // the fused fill is bf16 only
