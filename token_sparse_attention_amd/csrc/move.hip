@@ -289,8 +289,12 @@ __global__ __launch_bounds__(256) void scatter_inv_kernel(const T* __restrict__ 
                                                           const T* X, T* Y, int64_t L, int Hq, int64_t C) {
   constexpr int VPR = D * (int)sizeof(T) / 16;
   constexpr int TPB = 256 / VPR;                  // tokens per block
-  const int h = blockIdx.y, c = threadIdx.x % VPR;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x / VPR;
+  // token-major: the Hq blocks of one token tile are consecutive, so the rows of a token (all heads,
+  // Hq * d contiguous elements of X and Y) are read and written close together in time.  Head-major
+  // order (each head's tokens first) touched 256-byte pieces 8 KB apart: 0.605 against 0.559 ms at
+  // L = 131072, 0.181 against 0.148 ms at 32768.
+  const int h = (int)(blockIdx.x % (unsigned)Hq), c = threadIdx.x % VPR;
+  const int64_t t = (int64_t)(blockIdx.x / (unsigned)Hq) * TPB + threadIdx.x / VPR;
   if (t >= L) return;
   const uint4* O4 = reinterpret_cast<const uint4*>(Oh);
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
@@ -415,7 +419,7 @@ static hipError_t run_scatter(const void* Oh, const int32_t* idx, const int32_t*
   const size_t n = (size_t)L * Hq * VPR;
   if (inv) {
     constexpr int TPB = 256 / VPR;
-    const dim3 grid((unsigned)((L + TPB - 1) / TPB), (unsigned)Hq);
+    const dim3 grid((unsigned)((L + TPB - 1) / TPB * Hq));
     scatter_inv_kernel<T, D><<<grid, 256, 0, st>>>(static_cast<const T*>(Oh), inv, static_cast<const T*>(X),
                                                    static_cast<T*>(Y), L, Hq, C);
     return hipGetLastError();
