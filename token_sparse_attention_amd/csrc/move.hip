@@ -181,7 +181,8 @@ __global__ __launch_bounds__(kVtThreads) void gather_vt_bf16_kernel(const uint16
 }
 
 // The fused layer's V^T gather with its unselected-row fill in the same launch: blocks [0, ngather)
-// gather, the Hq * ceil(L / 256) blocks after them fill (the two touch disjoint memory).
+// gather, the Hq * ceil(L / 256) blocks after them fill (the two touch disjoint memory), token tile
+// outermost.
 template <int D>
 __global__ __launch_bounds__(256) void gather_vt_fill_bf16_kernel(const uint16_t* __restrict__ V,
                                                                   const int32_t* __restrict__ idx,
@@ -193,9 +194,9 @@ __global__ __launch_bounds__(256) void gather_vt_fill_bf16_kernel(const uint16_t
   if (blockIdx.x < ngather) {
     gather_vt_bf16_block<D, 256>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, lds);
   } else {
-    const int64_t f = blockIdx.x - ngather, per_head = (L + 255) / 256;
-    fill_unselected_block<uint16_t, D>(inv, X, Y, L, Hq, (int)(f / per_head), f % per_head,
-                                       reinterpret_cast<int32_t*>(lds));
+    // token-major, as the scatter: the Hq blocks of one 256-token tile are consecutive
+    const int64_t f = blockIdx.x - ngather;
+    fill_unselected_block<uint16_t, D>(inv, X, Y, L, Hq, (int)(f % Hq), f / Hq, reinterpret_cast<int32_t*>(lds));
   }
 }
 
