@@ -67,7 +67,7 @@ template <int D, int NT>
 constexpr int gather_lds_vectors() { return D * (NT / (D / 8)); }
 
 // The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
-// A block takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
+// A block of 256 threads takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
 // coalesced load into LDS, and a block whose tokens are all selected stops there.  Then VPR
 // consecutive lanes move one 16-byte chunk each of a row, so every store instruction writes whole
 // rows: whole cache lines, which the streaming hint needs.  Rows written one 16-byte chunk per
@@ -100,7 +100,6 @@ __device__ __forceinline__ void fill_unselected_block(const int32_t* __restrict_
     st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), reinterpret_cast<uint4*>(Y) + e);
   }
 }
-
 
 // bf16: a thread owns one 16-byte chunk (8 columns) of 8 consecutive compressed rows.  It loads that
 // chunk of the 8 gathered rows (16 threads cover a 256-byte row, so the loads stay coalesced) and
