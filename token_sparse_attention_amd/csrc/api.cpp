@@ -231,16 +231,23 @@ int run_layer(const tsa_shape* s, bool fixed_ratio, float sparsity, const void* 
   if (e == hipSuccess)
     e = launch_score(s->dtype, s->d, Q, K, s->L, s->Hq, s->Hkv, s->q, s_h, at<double2>(ws, g.partials),
                      at<double2>(ws, g.rowstat), st);
+  // a short row under tau: budget and selection in one launch
+  const bool merged = !fixed_ratio && radix_resident(s->L);
   if (fixed_ratio) {
     if (e == hipSuccess)
       e = launch_budget_ratio(sparsity, s->L, kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
+  } else if (merged) {
+    if (e == hipSuccess)
+      e = launch_layer_budget_select(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l,
+                                     budget_target(s->tau), kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, idx, inv,
+                                     st);
   } else {
     if (e == hipSuccess)
       e = launch_layer_score_budget(s_h, s->L, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l,
                                     budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl),
                                     kLp, kLp_dev, kLp_dev ? kLp_dev + 1 : nullptr, st);
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess && !merged)
     e = launch_select(s_h, s->L, s->Hq, kLp + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
                       at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
   // bf16 without block sparsity: the attention reads the query and key rows through idx and writes Y
@@ -536,11 +543,15 @@ int tsa_layer_varlen(const tsa_shape* s, int32_t B, const int64_t* cu_seqlens, c
     if (e == hipSuccess)
       e = launch_score(s->dtype, s->d, tok(Q, Hq, b), tok(K, Hkv, b), Lb, s->Hq, s->Hkv, s->q, s_h,
                        at<double2>(ws, g.partials), at<double2>(ws, g.rowstat), st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && radix_resident(Lb))
+      e = launch_layer_budget_select(s_h, Lb, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l,
+                                     budget_target(s->tau), kl, kLp_dev ? kLp_dev + 2 * b : nullptr,
+                                     kLp_dev ? kLp_dev + 2 * b + 1 : nullptr, idx, inv, st);
+    if (e == hipSuccess && !radix_resident(Lb))
       e = launch_layer_score_budget(s_h, Lb, s->Hq, at<double>(ws, g.S), at<double>(ws, g.tilesum), s_l,
                                     budget_target(s->tau), at<uint64_t>(ws, g.bhist), at<RadixCtl>(ws, g.bctl), kl,
                                     kLp_dev ? kLp_dev + 2 * b : nullptr, kLp_dev ? kLp_dev + 2 * b + 1 : nullptr, st);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !radix_resident(Lb))
       e = launch_select(s_h, Lb, s->Hq, kl + 1, at<uint64_t>(ws, g.shist), at<RadixCtl>(ws, g.sctl),
                         at<uint32_t>(ws, g.tcnt), at<uint32_t>(ws, g.toff), idx, inv, st);
     if (e == hipSuccess)

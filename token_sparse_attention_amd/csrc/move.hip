@@ -59,12 +59,9 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ Q, co
   }
 }
 
-// 16-byte LDS vectors of the bf16 V^T gather's transpose tile for NT threads: [d columns][rows / 8],
-// rows = 8 NT / (d / 8).  Two row groups per thread (256 rows, each column's run leaving as one
-// 512-byte store, 64 KB of LDS) measured 12% slower at L = 131072 than one: the LDS then allows only
-// 2 workgroups per CU instead of 5.
-template <int D, int NT>
-constexpr int gather_lds_vectors() { return D * (NT / (D / 8)); }
+// Compressed rows per block of the bf16 V^T gather (256 threads): 128 at d = 128, 256 at d = 64.
+template <int D>
+constexpr int vt_block_rows() { return 64 * (4 / (D / 64)); }
 
 // The rows no head selected: Y = X (or +0.0).  The fused layer's attention epilogue writes the rest.
 // A block of 256 threads takes 256 consecutive tokens of one head.  Their inverse-map entries are read with one
@@ -101,21 +98,24 @@ __device__ __forceinline__ void fill_unselected_block(const int32_t* __restrict_
   }
 }
 
-// bf16: a thread owns one 16-byte chunk (8 columns) of 8 consecutive compressed rows.  It loads that
-// chunk of the 8 gathered rows (16 threads cover a 256-byte row, so the loads stay coalesced) and
-// transposes the 8 x 8 block of 16-bit values in registers with byte permutes.  The resulting
-// 16-byte pieces (8 rows of one column) are regrouped through LDS, [column][row] with a XOR swizzle
-// of the piece slot, so that each column's run of TR rows leaves as contiguous 16-byte stores.
-template <int D, int NT>
+// bf16 V^T gather: Vht[h][c][i] = V[idx[h][i]][g][c] for rows i < L'.  No LDS: of a 256-thread
+// block, wave w takes 64 consecutive compressed rows and 8 of a row's 16-byte chunks (64 columns);
+// lane l loads chunk l % 8 of 8 consecutive rows (8 (l / 8) ..), so each load instruction reads 8
+// half-rows of 128 bytes, transposes that 8 x 8 block of 16-bit values in registers with byte
+// permutes, and stores one 16-byte piece (8 rows) per column.  A store instruction thus writes 8
+// columns x 64 rows: 8 whole 128-byte lines.  Measured against staging the transpose through LDS
+// behind a barrier (32/8 heads): 0.094 against 0.104 ms at L = 32768, 0.362 against 0.385 ms at
+// L = 131072.  Loading the next 64-row group before storing the current one did not help: this
+// kernel's reads and writes add up in HBM time (0.031 and 0.055 ms for each half alone at 32768),
+// and a layout with each block's output contiguous ([C / 128][d][128]) gained only 6-10%.
+template <int D>
 __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
-                                                     int64_t C, uint16_t* __restrict__ Vht, unsigned bid,
-                                                     uint4* tile) {     // LDS, gather_lds_vectors<D, NT>()
+                                                     int64_t C, uint16_t* __restrict__ Vht, unsigned bid) {
   constexpr int VPR = D / 8;            // 16-byte chunks per row
-  constexpr int NG = NT / VPR;          // groups of 8 rows per block
-  constexpr int TR = NG * 8;            // rows per block
-  constexpr int PPC = TR / 8;           // 16-byte pieces per column in the block (= NG)
-  // tile: [column][piece], piece slot swizzled
+  constexpr int WPR = D / 64;           // waves across one row's chunks
+  constexpr int TR = vt_block_rows<D>();
+  static_assert(TR == 64 * (4 / WPR), "four waves of 64 rows per block");
   // block -> (KV group, row tile, head of the group): the G heads of one (group, tile) pair are
   // consecutive blocks of one XCD (block index % 8), so its L2 serves the V rows they share
   const int G = Hq / Hkv;
@@ -125,22 +125,22 @@ __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict_
   if (pair >= ntiles * Hkv) return;
   const int g = (int)(pair % Hkv), h = g * G + slot % G;
   const int64_t Lp = Lp_dev[0];
-  const int64_t b0 = (pair / Hkv) * TR;
-  if (b0 >= Lp) return;
-  const int c = threadIdx.x % VPR, grp = threadIdx.x / VPR;
-  const int64_t r0 = b0 + grp * 8;
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int c = (w % WPR) * 8 + (l & 7);
+  const int64_t r0 = (pair / Hkv) * TR + 64 * (w / WPR) + 8 * (l >> 3);
+  if (r0 >= Lp) return;
   const uint4* V4 = reinterpret_cast<const uint4*>(V);
+  const int32_t* hidx = idx + (size_t)h * L;
   uint32_t v[8][4];
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int64_t i = r0 + u;
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (i < Lp) x = V4[((size_t)idx[(size_t)h * L + i] * Hkv + g) * VPR + c];
+    uint4 x = make_uint4(0, 0, 0, 0);   // rows at and past L' (columns of Vht past L') get zeros
+    if (r0 + u < Lp) x = V4[((size_t)hidx[r0 + u] * Hkv + g) * VPR + c];
     v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
   }
   // column 2j of the chunk is the low half of word j of every row, column 2j+1 the high half; word
-  // m of a column piece pairs rows 2m (low) and 2m+1 (high).  Piece grp of column col sits in slot
-  // grp ^ (col % PPC) of that column's LDS row.
+  // m of a column piece pairs rows 2m (low) and 2m+1 (high)
+  uint16_t* dst = Vht + ((size_t)h * D + 8 * c) * C + r0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     uint4 lo, hi;
@@ -152,31 +152,16 @@ __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict_
     hi.y = __builtin_amdgcn_perm(v[3][j], v[2][j], 0x07060302u);
     hi.z = __builtin_amdgcn_perm(v[5][j], v[4][j], 0x07060302u);
     hi.w = __builtin_amdgcn_perm(v[7][j], v[6][j], 0x07060302u);
-    const int col = 8 * c + 2 * j;
-    tile[col * PPC + (grp ^ (col % PPC))] = lo;
-    tile[(col + 1) * PPC + (grp ^ ((col + 1) % PPC))] = hi;
-  }
-  __syncthreads();
-  // each column's TR rows: PPC consecutive lanes store its PPC pieces contiguously
-  const int64_t nrows = Lp - b0 < TR ? Lp - b0 : TR;
-  for (int e = threadIdx.x; e < D * PPC; e += NT) {
-    const int col = e / PPC, q = e % PPC;
-    if ((int64_t)q * 8 >= nrows) continue;
-    st_stream(tile[col * PPC + (q ^ (col % PPC))], reinterpret_cast<uint4*>(Vht + ((size_t)h * D + col) * C + b0 + 8 * q));
+    st_stream(lo, reinterpret_cast<uint4*>(dst + (size_t)(2 * j) * C));
+    st_stream(hi, reinterpret_cast<uint4*>(dst + (size_t)(2 * j + 1) * C));
   }
 }
 
-// Threads of the stage call's V^T gather: 256 (128 rows per block at d = 128).  128 threads (64
-// rows, 16 KB of LDS) measured 1.5% faster at L = 131072 but 2-4% slower at 32768, 64 threads 15%
-// slower at both.
-constexpr int kVtThreads = 256;
-
 template <int D>
-__global__ __launch_bounds__(kVtThreads) void gather_vt_bf16_kernel(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
+__global__ __launch_bounds__(256) void gather_vt_bf16_kernel(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
                                                              const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
                                                              int64_t C, uint16_t* __restrict__ Vht) {
-  __shared__ uint4 tile[gather_lds_vectors<D, kVtThreads>()];
-  gather_vt_bf16_block<D, kVtThreads>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, tile);
+  gather_vt_bf16_block<D>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x);
 }
 
 // The fused layer's V^T gather with its unselected-row fill in the same launch: blocks [0, ngather)
@@ -189,13 +174,13 @@ __global__ __launch_bounds__(256) void gather_vt_fill_bf16_kernel(const uint16_t
                                                                   int Hkv, int64_t C, uint16_t* __restrict__ Vht,
                                                                   unsigned ngather, const int32_t* __restrict__ inv,
                                                                   const uint16_t* __restrict__ X, uint16_t* __restrict__ Y) {
-  __shared__ uint4 lds[gather_lds_vectors<D, 256>()];   // one role per block: the fill reuses it
+  __shared__ int32_t sinv[260];          // the fill's inverse-map entries and wave flags
   if (blockIdx.x < ngather) {
-    gather_vt_bf16_block<D, 256>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x, lds);
+    gather_vt_bf16_block<D>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, blockIdx.x);
   } else {
     // token-major, as the scatter: the Hq blocks of one 256-token tile are consecutive
     const int64_t f = blockIdx.x - ngather;
-    fill_unselected_block<uint16_t, D>(inv, X, Y, L, Hq, (int)(f % Hq), f / Hq, reinterpret_cast<int32_t*>(lds));
+    fill_unselected_block<uint16_t, D>(inv, X, Y, L, Hq, (int)(f % Hq), f / Hq, sinv);
   }
 }
 
@@ -207,15 +192,18 @@ __global__ __launch_bounds__(256) void gather_vt_fill_bf16_kernel(const uint16_t
 // the stores).  Block -> (KV group, row tile, head) as in the transposing kernel, so that one XCD's
 // L2 serves the K rows the group's heads share.
 template <int D>
-__global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                               const int32_t* __restrict__ idx,
-                                                               const int32_t* __restrict__ Lp_dev, int64_t L, int Hq,
-                                                               int Hkv, int64_t C, uint16_t* __restrict__ Qh,
-                                                               uint16_t* __restrict__ Kh) {
-  constexpr int VPR = D / 8, TRC = 256 / VPR;   // rows per block
+constexpr int rows_block_rows() { return 256 / (D / 8); }
+
+template <int D>
+__device__ __forceinline__ void gather_rows_bf16_block(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                       const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,
+                                                       int64_t C, uint16_t* __restrict__ Qh, uint16_t* __restrict__ Kh,
+                                                       unsigned bid) {
+  constexpr int VPR = D / 8, TRC = rows_block_rows<D>();   // rows per block
   const int G = Hq / Hkv;
   const int64_t ntiles = (L + TRC - 1) / TRC;
-  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int xcd = bid & 7, slot = bid >> 3;
   const int64_t pair = (int64_t)(slot / G) * 8 + xcd;
   if (pair >= ntiles * Hkv) return;
   const int g = (int)(pair % Hkv), h = g * G + slot % G;
@@ -230,6 +218,28 @@ __global__ __launch_bounds__(256) void gather_rows_bf16_kernel(const uint16_t* _
   if (Kh) kv = reinterpret_cast<const uint4*>(K)[(t * Hkv + g) * VPR + c];
   if (Qh) st_stream(qv, reinterpret_cast<uint4*>(Qh) + dst);
   if (Kh) st_stream(kv, reinterpret_cast<uint4*>(Kh) + dst);
+}
+
+// The stage call's bf16 gather in one launch: row-copy blocks (Q_hat, K_hat) and V^T blocks, in
+// groups of 8 consecutive blocks (one per XCD, so each role keeps its XCD mapping), the V^T groups
+// spread evenly among the row-copy groups.  The read-and-write row copies and the write-heavy
+// transposes then share the memory system over the whole launch instead of one after the other.
+template <int D>
+__global__ __launch_bounds__(256) void gather_qkv_bf16_kernel(const uint16_t* __restrict__ Q,
+                                                              const uint16_t* __restrict__ K,
+                                                              const uint16_t* __restrict__ V,
+                                                              const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ Lp_dev, int64_t L, int Hq,
+                                                              int Hkv, int64_t C, uint16_t* __restrict__ Qh,
+                                                              uint16_t* __restrict__ Kh, uint16_t* __restrict__ Vht,
+                                                              unsigned nrow_groups, unsigned nvt_groups) {
+  const uint64_t grp = blockIdx.x >> 3, tot = (uint64_t)nrow_groups + nvt_groups;
+  const unsigned xcd = blockIdx.x & 7;
+  // V^T groups before this one: floor(grp * nvt / tot); this group is a V^T group iff that count
+  // steps here, so the V^T groups take indices 0 .. nvt-1 and the row groups 0 .. nrow-1 in order
+  const uint64_t v0 = grp * nvt_groups / tot, v1 = (grp + 1) * nvt_groups / tot;
+  if (v1 > v0) gather_vt_bf16_block<D>(V, idx, Lp_dev, L, Hq, Hkv, C, Vht, (unsigned)(v0 * 8 + xcd));
+  else gather_rows_bf16_block<D>(Q, K, idx, Lp_dev, L, Hq, Hkv, C, Qh, Kh, (unsigned)((grp - v0) * 8 + xcd));
 }
 
 // V [L][Hkv][d] -> Vt [Hkv][d][C], columns L .. C-1 zero (the dense path's value layout).
@@ -351,27 +361,23 @@ static hipError_t run_gather(const void* Q, const void* K, const void* V, const 
   if constexpr (sizeof(T) == 2) {
     const auto Qt = static_cast<const uint16_t*>(Q), Kt = static_cast<const uint16_t*>(K);
     const auto Vt = static_cast<const uint16_t*>(V);
-    // the row copies of Q_hat and K_hat (no LDS, many waves), then the transposing V^T gather
+    // blocks of the transposing V^T gather, and (Q_hat, K_hat) of the row copies; both multiples of 8
+    constexpr int TR = vt_block_rows<D>(), TRC = rows_block_rows<D>();
+    const int64_t pairs = (L + TR - 1) / TR * Hkv, rpairs = (L + TRC - 1) / TRC * Hkv;
+    const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
+    const unsigned nrow = (unsigned)((rpairs + 7) / 8 * 8 * (Hq / Hkv));
     if (Qh || Kh) {
-      constexpr int TRC = 256 / (D / 8);
-      const int64_t rpairs = (L + TRC - 1) / TRC * Hkv;
-      const unsigned nrow = (unsigned)((rpairs + 7) / 8 * 8 * (Hq / Hkv));
-      gather_rows_bf16_kernel<D><<<nrow, 256, 0, st>>>(Qt, Kt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Qh),
-                                                       static_cast<uint16_t*>(Kh));
-    }
-    if (Y) {
-      constexpr int TR = 256 / (D / 8) * 8;
-      const int64_t pairs = (L + TR - 1) / TR * Hkv;
-      const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
+      if (Y) return hipErrorInvalidValue;   // the fused layer gathers V^T only
+      gather_qkv_bf16_kernel<D><<<nrow + nblk, 256, 0, st>>>(Qt, Kt, Vt, idx, Lp_dev, L, Hq, Hkv, C,
+                                                             static_cast<uint16_t*>(Qh), static_cast<uint16_t*>(Kh),
+                                                             static_cast<uint16_t*>(Vht), nrow / 8, nblk / 8);
+    } else if (Y) {
       const unsigned nfill = (unsigned)((L + 255) / 256 * Hq);
       gather_vt_fill_bf16_kernel<D><<<nblk + nfill, 256, 0, st>>>(Vt, idx, Lp_dev, L, Hq, Hkv, C,
                                                                   static_cast<uint16_t*>(Vht), nblk, inv,
                                                                   static_cast<const uint16_t*>(X), static_cast<uint16_t*>(Y));
     } else {
-      constexpr int TR = kVtThreads / (D / 8) * 8;
-      const int64_t pairs = (L + TR - 1) / TR * Hkv;
-      const unsigned nblk = (unsigned)((pairs + 7) / 8 * 8 * (Hq / Hkv));
-      gather_vt_bf16_kernel<D><<<nblk, kVtThreads, 0, st>>>(Vt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Vht));
+      gather_vt_bf16_kernel<D><<<nblk, 256, 0, st>>>(Vt, idx, Lp_dev, L, Hq, Hkv, C, static_cast<uint16_t*>(Vht));
     }
   } else {
     if (Y) return hipErrorInvalidValue;   // the fused fill is bf16 only

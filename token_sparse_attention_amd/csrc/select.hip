@@ -250,6 +250,10 @@ constexpr int kResBits = 11, kResBins = 1 << kResBits;
 
 bool radix_resident(int64_t L) { return L <= kResidentMax; }
 
+// Once at most this many keys share the prefix fixed so far, one wave ranks them directly instead
+// of running the remaining digit passes.
+constexpr int kResFinish = 64;
+
 // Two histograms: while wave 0 searches one pass's histogram, the other waves clear the next one's.
 template <bool MASS>
 struct ResShared {
@@ -257,6 +261,9 @@ struct ResShared {
   uint64_t hw[2][MASS ? kResBins : 1];       // weights (budget)
   uint32_t rmin[kResWaves], rmax[kResWaves], rcnt[kResWaves];
   uint64_t rw[kResWaves];
+  uint32_t fkey[kResFinish];                 // the keys under the prefix, for the direct ranking
+  uint64_t fw[MASS ? kResFinish : 1];        // and their weights (budget)
+  uint32_t fcnt;
   RadixCtl ctl;
 };
 
@@ -354,6 +361,56 @@ __device__ void res_find(ResShared<MASS>& sh, int buf, int nbins, int width, uin
   }
 }
 
+// The remaining digits at once, when n <= kResFinish keys share the prefix fixed so far: every thread
+// puts its keys under the prefix into a list, then wave 0 ranks the n keys against each other.  The
+// crossing key is the smallest one whose cumulative weight, counting every key equal to it,
+// reaches T: the same key, counts and weights the remaining passes would find.  Ends with the
+// result in sh.ctl, read after a barrier.
+template <int NK, bool MASS>
+__device__ void res_finish(const uint32_t (&key)[NK], int64_t L, int done, uint32_t prefix, uint64_t cb,
+                           uint64_t wb, uint64_t T, ResShared<MASS>& sh) {
+  const int64_t t0 = (int64_t)NK * threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    uint32_t k = key[i];
+    if (MASS) asm volatile("" : "+v"(k));             // weights computed here, not hoisted (registers)
+    if (t0 + i < L && (k >> (32 - done)) == prefix) {
+      const uint32_t pos = atomicAdd(&sh.fcnt, 1u);   // below kResFinish: n keys share the prefix
+      sh.fkey[pos] = k;
+      if (MASS) sh.fw[pos] = weight_of<true>(k);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x, n = (int)sh.fcnt;
+    const uint32_t kk = lane < n ? sh.fkey[lane] : 0u;
+    uint32_t ltc = 0, eqc = 0;
+    uint64_t ltw = 0, eqw = 0;
+#pragma unroll 1
+    for (int j = 0; j < n; ++j) {
+      const uint32_t kj = sh.fkey[j];
+      const uint64_t wj = MASS ? sh.fw[j] : 1ull;
+      if (kj < kk) { ++ltc; ltw += wj; }
+      if (kj == kk) { ++eqc; eqw += wj; }
+    }
+    const bool ok = lane < n && wb + ltw + eqw >= T;
+    uint32_t v = ok ? kk : 0xFFFFFFFFu;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor(v, o, kWave));
+    const uint64_t hit = __ballot(ok && kk == v);
+    if (hit == 0) {
+      if (lane == 0) sh.ctl.none = 1;
+    } else if (lane == __ffsll((long long)hit) - 1) {
+      sh.ctl.prefix = v;
+      sh.ctl.none = 0;
+      sh.ctl.cnt_below = cb + ltc;
+      sh.ctl.w_below = wb + ltw;
+      sh.ctl.n_bin = eqc;
+    }
+  }
+  __syncthreads();
+}
+
 // The key where the ascending cumulative weight of the row first reaches T (T >= 1), with the
 // count and weight of the keys below it and the number of keys equal to it.  Thread j holds keys
 // NK j .. NK j + NK - 1 (those at or past L are absent).  Every thread returns the same result.
@@ -386,6 +443,7 @@ __device__ ResResult resident_threshold(const uint32_t (&key)[NK], int64_t L, ui
     sh.rmax[w] = kmax;
     sh.rw[w] = wt;
   }
+  if (tid == 0) sh.fcnt = 0;
   res_clear<MASS>(sh, 0, 0);
   __syncthreads();
   uint64_t wtot = 0;
@@ -434,6 +492,18 @@ __device__ ResResult resident_threshold(const uint32_t (&key)[NK], int64_t L, ui
     wb = sh.ctl.w_below;
     n_eq = sh.ctl.n_bin;
     done += width;
+    if (done < 32 && n_eq <= (uint64_t)kResFinish) {   // block-uniform: read from LDS after a barrier
+      res_finish<NK, MASS>(key, L, done, prefix, cb, wb, T, sh);
+      if (sh.ctl.none) {
+        r.none = 1;
+        return r;
+      }
+      prefix = sh.ctl.prefix;
+      cb = sh.ctl.cnt_below;
+      wb = sh.ctl.w_below;
+      n_eq = sh.ctl.n_bin;
+      done = 32;
+    }
   }
   r.key = prefix;
   r.cnt_below = cb;
@@ -458,19 +528,13 @@ __device__ __forceinline__ void load_keys(const float* __restrict__ row, int64_t
   }
 }
 
-// Budget over one row.  FROM_S: s_l is first formed from the head sums S and their tile sums exactly
-// as launch_layer_score forms it (same total, same division) and stored.
+// The budget of one row by the whole workgroup: k (every thread returns it).  FROM_S: s_l is first
+// formed from the head sums S and their tile sums (as launch_layer_score does) and, with write_sl,
+// stored to s_l_out.
 template <int NK, bool FROM_S>
-__global__ __launch_bounds__(kResThreads) void budget_resident_kernel(const float* __restrict__ s_l_in,
-                                                                      const double* __restrict__ S,
-                                                                      const double* __restrict__ tile_sum,
-                                                                      int64_t ntiles, float* __restrict__ s_l_out,
-                                                                      int64_t L, uint64_t T,
-                                                                      int32_t* __restrict__ kLp_ws,
-                                                                      int32_t* __restrict__ k_out,
-                                                                      int32_t* __restrict__ Lp_out) {
-  __shared__ ResShared<true> sh;
-  __shared__ double red[4];
+__device__ __forceinline__ int64_t budget_resident_row(const float* __restrict__ s_l_in, const double* __restrict__ S,
+                                       const double* __restrict__ tile_sum, int64_t ntiles, float* __restrict__ s_l_out,
+                                       bool write_sl, int64_t L, uint64_t T, ResShared<true>& sh, double* red) {
   uint32_t key[NK];
   const int64_t t0 = (int64_t)NK * threadIdx.x;
   if constexpr (FROM_S) {
@@ -480,7 +544,7 @@ __global__ __launch_bounds__(kResThreads) void budget_resident_kernel(const floa
       key[i] = 0u;
       if (t0 + i < L) {
         const float v = (float)(S[t0 + i] / total);
-        s_l_out[t0 + i] = v;
+        if (write_sl) s_l_out[t0 + i] = v;
         key[i] = __float_as_uint(v);
       }
     }
@@ -497,11 +561,28 @@ __global__ __launch_bounds__(kResThreads) void budget_resident_kernel(const floa
       k = (int64_t)r.cnt_below + (int64_t)((T - r.w_below + V - 1) / V);
     }
   }
-  if (threadIdx.x == 0) {
-    if (kLp_ws) { kLp_ws[0] = (int32_t)k; kLp_ws[1] = (int32_t)(L - k); }
-    if (k_out) k_out[0] = (int32_t)k;
-    if (Lp_out) Lp_out[0] = (int32_t)(L - k);
-  }
+  return k;
+}
+
+__device__ __forceinline__ void write_keep(int64_t k, int64_t L, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out) {
+  if (kLp_ws) { kLp_ws[0] = (int32_t)k; kLp_ws[1] = (int32_t)(L - k); }
+  if (k_out) k_out[0] = (int32_t)k;
+  if (Lp_out) Lp_out[0] = (int32_t)(L - k);
+}
+
+template <int NK, bool FROM_S>
+__global__ __launch_bounds__(kResThreads) void budget_resident_kernel(const float* __restrict__ s_l_in,
+                                                                      const double* __restrict__ S,
+                                                                      const double* __restrict__ tile_sum,
+                                                                      int64_t ntiles, float* __restrict__ s_l_out,
+                                                                      int64_t L, uint64_t T,
+                                                                      int32_t* __restrict__ kLp_ws,
+                                                                      int32_t* __restrict__ k_out,
+                                                                      int32_t* __restrict__ Lp_out) {
+  __shared__ ResShared<true> sh;
+  __shared__ double red[4];
+  const int64_t k = budget_resident_row<NK, FROM_S>(s_l_in, S, tile_sum, ntiles, s_l_out, true, L, T, sh, red);
+  if (threadIdx.x == 0) write_keep(k, L, kLp_ws, k_out, Lp_out);
 }
 
 template <bool FROM_S>
@@ -700,19 +781,15 @@ __global__ __launch_bounds__(256) void select_write_kernel(const float* __restri
 
 // Selection over one head's row per workgroup: the threshold key V = the (k+1)-th smallest score
 // (k = L - L'), every key above it plus the lowest-index ties at it, compacted in ascending order.
+// The selection of one row by the whole workgroup, for a keep count Lp known to every thread.
 template <int NK>
-__global__ __launch_bounds__(kResThreads) void select_resident_kernel(const float* __restrict__ s_h, int64_t L,
-                                                                      const int32_t* __restrict__ Lp_dev,
-                                                                      int32_t* __restrict__ idx,
-                                                                      int32_t* __restrict__ inv) {
-  __shared__ ResShared<false> sh;
-  __shared__ uint64_t smask[kResThreads];
-  __shared__ uint32_t sbase[kResThreads];
-  const int h = blockIdx.x, tid = threadIdx.x;
+__device__ __forceinline__ void select_resident_row(const float* __restrict__ row, int64_t L, int64_t Lp, int32_t* __restrict__ irow,
+                                    int32_t* __restrict__ vrow, ResShared<false>& sh, uint64_t* smask,
+                                    uint32_t* sbase) {   // LDS, kResThreads entries each
+  const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)NK * tid;
   uint32_t key[NK];
-  load_keys<NK>(s_h + (size_t)h * L, L, key);
-  const int64_t Lp = Lp_dev[0];
+  load_keys<NK>(row, L, key);
   uint32_t V = 0xFFFFFFFFu;             // L' = 0: no key is above it or equal to it
   uint64_t take_eq = 0;
   if (Lp > 0) {
@@ -738,8 +815,6 @@ __global__ __launch_bounds__(kResThreads) void select_resident_kernel(const floa
   smask[tid] = m;
   sbase[tid] = base;
   __syncthreads();
-  int32_t* irow = idx + (size_t)h * L;
-  int32_t* vrow = inv ? inv + (size_t)h * L : nullptr;
   for (int64_t e = tid; e < L; e += kResThreads) {
     const int owner = (int)(e / NK), bit = (int)(e % NK);
     const uint64_t mo = smask[owner];
@@ -748,6 +823,49 @@ __global__ __launch_bounds__(kResThreads) void select_resident_kernel(const floa
     if (sel) irow[pos] = (int32_t)e;
     if (vrow) vrow[e] = sel ? pos : -1;
   }
+}
+
+template <int NK>
+__global__ __launch_bounds__(kResThreads) void select_resident_kernel(const float* __restrict__ s_h, int64_t L,
+                                                                      const int32_t* __restrict__ Lp_dev,
+                                                                      int32_t* __restrict__ idx,
+                                                                      int32_t* __restrict__ inv) {
+  __shared__ ResShared<false> sh;
+  __shared__ uint64_t smask[kResThreads];
+  __shared__ uint32_t sbase[kResThreads];
+  const int h = blockIdx.x;
+  select_resident_row<NK>(s_h + (size_t)h * L, L, Lp_dev[0], idx + (size_t)h * L, inv ? inv + (size_t)h * L : nullptr,
+                          sh, smask, sbase);
+}
+
+struct SelectShared {
+  ResShared<false> r;
+  uint64_t smask[kResThreads];
+  uint32_t sbase[kResThreads];
+};
+union BudgetSelectShared {   // budget first, then selection
+  ResShared<true> b;
+  SelectShared s;
+};
+
+// Budget and selection of a short layer in one launch of Hq workgroups: each forms s_l and runs the
+// budget itself (the same arithmetic on the same values, so every workgroup finds the same k), then
+// selects its head's L - k tokens; workgroup 0 also stores s_l, k and L'.  One launch and one
+// dependency fewer than the budget's single workgroup followed by the selection.
+template <int NK, bool FROM_S>
+__global__ __launch_bounds__(kResThreads) void budget_select_resident_kernel(
+    const float* __restrict__ s_h, const float* __restrict__ s_l_in, const double* __restrict__ S,
+    const double* __restrict__ tile_sum, int64_t ntiles, float* __restrict__ s_l_out, int64_t L, uint64_t T,
+    int32_t* __restrict__ kLp_ws, int32_t* __restrict__ k_out, int32_t* __restrict__ Lp_out,
+    int32_t* __restrict__ idx, int32_t* __restrict__ inv) {
+  __shared__ BudgetSelectShared sh;
+  __shared__ double red[4];
+  const int h = blockIdx.x;
+  const int64_t k = budget_resident_row<NK, FROM_S>(s_l_in, S, tile_sum, ntiles, s_l_out, h == 0, L, T, sh.b, red);
+  if (h == 0 && threadIdx.x == 0) write_keep(k, L, kLp_ws, k_out, Lp_out);
+  __syncthreads();   // the selection reuses the budget's LDS
+  select_resident_row<NK>(s_h + (size_t)h * L, L, L - k, idx + (size_t)h * L, inv ? inv + (size_t)h * L : nullptr,
+                          sh.s.r, sh.s.smask, sh.s.sbase);
 }
 
 static hipError_t launch_select_resident(const float* s_h, int64_t L, int Hq, const int32_t* Lp_dev, int32_t* idx,
@@ -773,6 +891,32 @@ hipError_t launch_select(const float* s_h, int64_t L, int Hq, const int32_t* Lp_
   select_count_kernel<<<sgrid, 256, 0, st>>>(s_h, L, Lp_dev, hist, ctl, tile_cnt);
   select_scan_kernel<<<(unsigned)Hq, 64, 0, st>>>(tile_cnt, nt, L, Lp_dev, ctl, tile_off);
   select_write_kernel<<<sgrid, 256, 0, st>>>(s_h, L, Lp_dev, ctl, tile_off, idx, inv);
+  return hipGetLastError();
+}
+
+// Layer score, budget and selection of a resident row (at most kResidentMax tokens).  The layer
+// score's kernels run as in launch_layer_score_budget; budget and selection then take one launch.
+hipError_t launch_layer_budget_select(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum, float* s_l,
+                                      uint64_t target, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out, int32_t* idx,
+                                      int32_t* inv, hipStream_t st) {
+  int64_t ntiles = 0;
+  if (L > 4 * kResThreads) {
+    const hipError_t e = launch_layer_score(s_h, L, Hq, S, tile_sum, s_l, st);
+    if (e != hipSuccess) return e;
+  } else {
+    ntiles = layer_tiles(L) - 1;
+    layer_sum_kernel<<<(unsigned)ntiles, 256, 0, st>>>(s_h, L, Hq, S, tile_sum);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+#define TSA_BUDGET_SELECT(NK, FS) \
+  budget_select_resident_kernel<NK, FS><<<(unsigned)Hq, kResThreads, 0, st>>>(s_h, s_l, S, tile_sum, ntiles, s_l, L, \
+                                                                              target, kLp_ws, k_out, Lp_out, idx, inv)
+  if (L <= 4 * kResThreads) TSA_BUDGET_SELECT(4, true);
+  else if (L <= 8 * kResThreads) TSA_BUDGET_SELECT(8, false);
+  else if (L <= 16 * kResThreads) TSA_BUDGET_SELECT(16, false);
+  else TSA_BUDGET_SELECT(32, false);
+#undef TSA_BUDGET_SELECT
   return hipGetLastError();
 }
 

@@ -56,6 +56,11 @@ int64_t select_tiles(int64_t L);
 hipError_t launch_select(const float* s_h, int64_t L, int Hq, const int32_t* Lp_dev,
                          uint64_t* hist, RadixCtl* ctl, uint32_t* tile_cnt, uint32_t* tile_off,
                          int32_t* idx, int32_t* inv, hipStream_t st);
+// For a resident row only (radix_resident(L)): launch_layer_score_budget followed by launch_select
+// with L' from the budget (same s_l, k, L', idx and inv), budget and selection in one launch.
+hipError_t launch_layer_budget_select(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum, float* s_l,
+                                      uint64_t target, int32_t* kLp_ws, int32_t* k_out, int32_t* Lp_out, int32_t* idx,
+                                      int32_t* inv, hipStream_t st);
 
 // ---- move.hip -----------------------------------------------------------------------------------
 // With Y (bf16 only), the same launch also writes the rows outside every selection:
