@@ -90,3 +90,61 @@ def test_budget_exact(gpu, L, kind):
         k, Lp = kl.tolist()
         assert k + Lp == L
         assert k == exact_budget(s_l, t32), (kind, L, tau, k)
+
+
+def cluster_row(L, n, seed):
+    """A row whose middle ranks are a cluster of n keys sharing their leading bits, with exact ties
+    (1 + j * 2^-20 for j in 0..7), between n_hi large keys above and small keys below: the
+    one-workgroup select ranks the cluster directly once at most 64 keys share the prefix, and runs
+    another digit pass first for 65."""
+    r = np.random.default_rng(seed)
+    s = r.random(L) * 0.25                                   # small keys
+    pos = r.permutation(L)
+    n_hi = L // 2 - n // 2
+    s[pos[:n_hi]] = 2.0 + r.random(n_hi) * 2.0               # large keys
+    s[pos[n_hi:n_hi + n]] = 1.0 + r.integers(0, 8, size=n) * 2.0 ** -20
+    return s.astype(np.float32), n_hi
+
+
+@pytest.mark.parametrize("L", [4097, 20001, 32768])
+@pytest.mark.parametrize("n", [2, 63, 64, 65, 200])
+def test_select_cluster(gpu, L, n):
+    s, n_hi = cluster_row(L, n, seed=L + n)
+    Hq = 1
+    s_h = torch.from_numpy(s[None, :].copy()).to(gpu)
+    shape = binding.shape(L, Hq, 1, 128, 1, 0.01, "bf16")
+    ws = binding.workspace(binding.stage_workspace_bytes(shape), gpu)
+    # L' inside the cluster: its first, middle and last keys, and the ranks just outside it
+    for Lp in sorted({n_hi, n_hi + 1, n_hi + n // 2, n_hi + n - 1, n_hi + n, n_hi + n + 1}):
+        idx = torch.full((Hq, L), -7, dtype=torch.int32, device=gpu)
+        inv = torch.full((Hq, L), -7, dtype=torch.int32, device=gpu)
+        binding.select(shape, s_h, torch.tensor([Lp], dtype=torch.int32, device=gpu), idx, inv, ws)
+        got, gi = idx.cpu().numpy(), inv.cpu().numpy()
+        want = oracle.select(s[None, :].astype(np.float64), Lp)
+        assert (got[:, :Lp] == want).all(), (L, n, Lp)
+        w = np.full(L, -1)
+        w[want[0]] = np.arange(Lp)
+        assert (gi[0] == w).all(), (L, n, Lp)
+
+
+@pytest.mark.parametrize("L", [4097, 20001, 32768])
+@pytest.mark.parametrize("n", [2, 63, 64, 65, 200])
+def test_budget_cluster(gpu, L, n):
+    # ascending mass: the budget's crossing falls among the cluster when tau lies inside its mass
+    s, n_hi = cluster_row(L, n, seed=L + 7 * n)
+    tot = s.astype(np.float64).sum()
+    s_l = (s.astype(np.float64) / tot).astype(np.float32)
+    d_sl = torch.from_numpy(s_l).to(gpu)
+    v = np.sort(s_l.astype(np.float64))
+    below = v[: L - n_hi - n].sum()                          # the small keys
+    cl = v[L - n_hi - n: L - n_hi]
+    for frac in (0.0, 0.3, 0.5, 0.99):
+        tau = below + frac * cl.sum() + (1e-9 if frac == 0.0 else 0.0)
+        t32 = float(np.float32(tau))
+        shape = binding.shape(L, 1, 1, 128, 1, t32, "bf16")
+        ws = binding.workspace(binding.stage_workspace_bytes(shape), gpu)
+        kl = torch.full((2,), -5, dtype=torch.int32, device=gpu)
+        binding.budget(shape, d_sl, kl[0:1], kl[1:2], ws)
+        k, Lp = kl.tolist()
+        assert k + Lp == L
+        assert k == exact_budget(s_l, t32), (L, n, frac, k)
