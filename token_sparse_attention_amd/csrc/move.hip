@@ -107,7 +107,7 @@ __device__ __forceinline__ void fill_unselected_block(const int32_t* __restrict_
 // behind a barrier (32/8 heads): 0.094 against 0.104 ms at L = 32768, 0.362 against 0.385 ms at
 // L = 131072.  Loading the next 64-row group before storing the current one did not help: this
 // kernel's reads and writes add up in HBM time (0.031 and 0.055 ms for each half alone at 32768),
-// and a layout with each block's output contiguous ([C / 128][d][128]) gained only 6-10%.
+// and a layout with each block's output contiguous ([C / 128][d][128]) was no faster than this one.
 template <int D>
 __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict__ V, const int32_t* __restrict__ idx,
                                                      const int32_t* __restrict__ Lp_dev, int64_t L, int Hq, int Hkv,

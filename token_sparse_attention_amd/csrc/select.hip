@@ -779,9 +779,9 @@ __global__ __launch_bounds__(256) void select_write_kernel(const float* __restri
   }
 }
 
-// Selection over one head's row per workgroup: the threshold key V = the (k+1)-th smallest score
-// (k = L - L'), every key above it plus the lowest-index ties at it, compacted in ascending order.
-// The selection of one row by the whole workgroup, for a keep count Lp known to every thread.
+// Selection over one head's row by the whole workgroup, for a keep count Lp known to every thread:
+// the threshold key V = the (k+1)-th smallest score (k = L - L'), every key above it plus the
+// lowest-index ties at it, compacted in ascending order.
 template <int NK>
 __device__ __forceinline__ void select_resident_row(const float* __restrict__ row, int64_t L, int64_t Lp, int32_t* __restrict__ irow,
                                     int32_t* __restrict__ vrow, ResShared<false>& sh, uint64_t* smask,
