@@ -430,6 +430,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
   const uint16_t* xrow = (DENSE || FUSED) && a.X
       ? reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.X) + qo_off * 2 + (size_t)qrow_i * q_rs)
       : nullptr;
+  // the residual row first, every load before any store: Y may alias X (in place), which would
+  // otherwise make each load wait for the store before it (16 round trips per wave)
+  uint2 xr[DT][4];
+  if (xrow) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) xr[dt][rq] = *reinterpret_cast<const uint2*>(xrow + 32 * dt + 8 * rq + 4 * hf);
+  }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -443,7 +452,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
         for (int x = 0; x < 4; ++x) v[x] = bf16_to_f32(f32_to_bf16(v[x]));
       }
       if (xrow) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(xrow + d0);
+        const uint2 xv = xr[dt][rq];
         v[0] += bf16_to_f32((uint16_t)xv.x);
         v[1] += bf16_to_f32((uint16_t)(xv.x >> 16));
         v[2] += bf16_to_f32((uint16_t)xv.y);
@@ -547,10 +556,13 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   float* Op = static_cast<float*>(a.O);
   const float* Xp = static_cast<const float*>(a.X);
   const size_t orow = q_row(qi);
+  float xr[DPT];                        // residual loads before any store (Y may alias X)
+#pragma unroll
+  for (int u = 0; u < DPT; ++u) xr[u] = DENSE && Xp ? Xp[orow + part + TPR * u] : 0.f;
 #pragma unroll
   for (int u = 0; u < DPT; ++u) {
     float v = acc[u] * inv_l;
-    if (DENSE && Xp) v += Xp[orow + part + TPR * u];
+    if (DENSE && Xp) v += xr[u];
     Op[orow + part + TPR * u] = v;
   }
 }
