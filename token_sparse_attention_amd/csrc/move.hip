@@ -88,13 +88,26 @@ __device__ __forceinline__ void fill_unselected_block(const int32_t* __restrict_
   __syncthreads();
   if ((sinv[256] | sinv[257] | sinv[258] | sinv[259]) == 0) return;   // every token of the block is selected
   const uint4* X4 = reinterpret_cast<const uint4*>(X);
+  // in batches of 8 rows, every load of a batch before its stores: with one branch per row, a load
+  // placed after the previous row's store waited for it (one memory round trip per row)
+  constexpr int NB = VPR < 8 ? VPR : 8;
 #pragma unroll
-  for (int p = 0; p < VPR; ++p) {
-    const int r = p * TPB + (int)threadIdx.x / VPR;
-    const int64_t t = base + r;
-    if (t >= L || sinv[r] >= 0) continue;
-    const size_t e = ((size_t)t * Hq + h) * VPR + c;
-    st_stream(X4 ? ld_stream(&X4[e]) : make_uint4(0, 0, 0, 0), reinterpret_cast<uint4*>(Y) + e);
+  for (int p0 = 0; p0 < VPR; p0 += NB) {
+    uint4 xv[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int r = (p0 + b) * TPB + (int)threadIdx.x / VPR;
+      const int64_t t = base + r;
+      xv[b] = make_uint4(0, 0, 0, 0);
+      if (X4 && t < L && sinv[r] < 0) xv[b] = ld_stream(&X4[((size_t)t * Hq + h) * VPR + c]);
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int r = (p0 + b) * TPB + (int)threadIdx.x / VPR;
+      const int64_t t = base + r;
+      if (t >= L || sinv[r] >= 0) continue;
+      st_stream(xv[b], reinterpret_cast<uint4*>(Y) + ((size_t)t * Hq + h) * VPR + c);
+    }
   }
 }
 
@@ -131,12 +144,29 @@ __device__ __forceinline__ void gather_vt_bf16_block(const uint16_t* __restrict_
   if (r0 >= Lp) return;
   const uint4* V4 = reinterpret_cast<const uint4*>(V);
   const int32_t* hidx = idx + (size_t)h * L;
+  // the 8 tokens first, then the 8 rows, with no per-row condition on a full group of 8: a load under
+  // a per-row branch, or followed by a per-row select of its value, waited for every load before
+  // it, so a thread's 8 token and 8 row loads ran one after another.  The group that crosses L'
+  // reads row L' - 1 in place of the rows past it and zeroes them.
+  int32_t tok[8];
   uint32_t v[8][4];
+  if (r0 + 8 <= Lp) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    uint4 x = make_uint4(0, 0, 0, 0);   // rows at and past L' (columns of Vht past L') get zeros
-    if (r0 + u < Lp) x = V4[((size_t)hidx[r0 + u] * Hkv + g) * VPR + c];
-    v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+    for (int u = 0; u < 8; ++u) tok[u] = hidx[r0 + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint4 x = V4[((size_t)tok[u] * Hkv + g) * VPR + c];
+      v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tok[u] = hidx[r0 + u < Lp ? r0 + u : Lp - 1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      uint4 x = V4[((size_t)tok[u] * Hkv + g) * VPR + c];
+      if (r0 + u >= Lp) x = make_uint4(0, 0, 0, 0);   // columns of Vht past L' get zeros
+      v[u][0] = x.x; v[u][1] = x.y; v[u][2] = x.z; v[u][3] = x.w;
+    }
   }
   // column 2j of the chunk is the low half of word j of every row, column 2j+1 the high half; word
   // m of a column piece pairs rows 2m (low) and 2m+1 (high)
