@@ -195,10 +195,25 @@ __global__ __launch_bounds__(256) void radix_hist_kernel(const float* __restrict
   const int shift_digit = 24 - 8 * pass;
   const float* kseg = keys + (size_t)seg * seg_stride;
   const int64_t base = (int64_t)blockIdx.x * kHistTile;
-  for (int u = 0; u < kHistTile / 256; ++u) {
+  // every key of the thread first, then the counting: a load under a per-key branch waited for the
+  // loads before it (one memory round trip per key)
+  constexpr int KPT = kHistTile / 256;
+  uint32_t kv[KPT];
+  if (base + kHistTile <= L) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) kv[u] = __float_as_uint(kseg[base + u * 256 + threadIdx.x]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int64_t t = base + u * 256 + threadIdx.x;
+      kv[u] = t < L ? __float_as_uint(kseg[t]) : 0u;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < KPT; ++u) {
     const int64_t t = base + u * 256 + threadIdx.x;
     if (t >= L) break;
-    const uint32_t key = __float_as_uint(kseg[t]);
+    const uint32_t key = kv[u];
     if (pass > 0 && (key >> (32 - 8 * pass)) != cur.prefix) continue;
     const uint32_t dg = (key >> shift_digit) & 0xFFu;
     atomicAdd((unsigned long long*)&hc[dg], 1ull);
@@ -538,12 +553,21 @@ __device__ __forceinline__ int64_t budget_resident_row(const float* __restrict__
   uint32_t key[NK];
   const int64_t t0 = (int64_t)NK * threadIdx.x;
   if constexpr (FROM_S) {
+    // the head sums first (no per-element branch between the loads), then the divisions
+    double sv[NK];
+    if (t0 + NK <= L) {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) sv[i] = S[t0 + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NK; ++i) sv[i] = t0 + i < L ? S[t0 + i] : 0.0;
+    }
     const double total = tile_total(tile_sum, ntiles, red);
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
       key[i] = 0u;
       if (t0 + i < L) {
-        const float v = (float)(S[t0 + i] / total);
+        const float v = (float)(sv[i] / total);
         if (write_sl) s_l_out[t0 + i] = v;
         key[i] = __float_as_uint(v);
       }
