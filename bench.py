@@ -637,7 +637,8 @@ def tau_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
         ev = sweep_evidence(cfg, s, Q, K, V, X, lambda Yn, kl: binding.layer(s, Q, K, V, X, Yn, kl, ws),
                             lambda: _stage_selection(cfg, s, Q, K, lambda sl, kl, w: binding.budget(
                                 s, sl, kl[0:1], kl[1:2], w)), seed=int(tau * 100))
-        out.append({"tau": tau, "k": k, "L_keep": Lp, "pruned_frac": round(k / cfg.L, 4), "layer_ms": round(ms, 3),
+        out.append({"supplementary": True, "tau": tau, "k": k, "L_keep": Lp, "pruned_frac": round(k / cfg.L, 4),
+                    "layer_ms": round(ms, 3),
                     "speedup_vs_dense": round(dense_ms / ms, 3)})
         pend.append((out[-1], dict(ev, kind="tau", tau=tau)))
         del ws
@@ -658,7 +659,7 @@ def ratio_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
         ev = sweep_evidence(cfg, s, Q, K, V, X, lambda Yn, kl: binding.layer_ratio(s, sp, Q, K, V, X, Yn, kl, ws),
                             lambda: _stage_selection(cfg, s, Q, K, lambda sl, kl, w: binding.budget_ratio(
                                 s, sp, kl[0:1], kl[1:2])), seed=int(sp * 100))
-        out.append({"sparsity": sp, "k": k, "L_keep": Lp, "layer_ms": round(ms, 3),
+        out.append({"supplementary": True, "sparsity": sp, "k": k, "L_keep": Lp, "layer_ms": round(ms, 3),
                     "speedup_vs_dense": round(dense_ms / ms, 3)})
         pend.append((out[-1], dict(ev, kind="ratio", sparsity=sp)))
     del ws, Y
@@ -706,7 +707,8 @@ def block_sparse_sweep(cfg, Q, K, V, X, dense_ms, steps, warmup, stream):
                                 lambda: idx, heads=BLOCK_PARITY_HEADS, rows_per_head=16, seed=int(gamma * 10))
             lists = {h: [blist[h, I, :int(bcnt[h, I])].cpu().numpy().astype(np.int64) for I in range(nb)]
                      for h in BLOCK_PARITY_HEADS}
-            out.append({"tau": tau, "gamma": gamma, "L_keep": Lp, "kept_block_frac": round(kept, 4),
+            out.append({"supplementary": True, "tau": tau, "gamma": gamma, "L_keep": Lp,
+                        "kept_block_frac": round(kept, 4),
                         "layer_ms": round(ms, 3), "speedup_vs_dense": round(dense_ms / ms, 3)})
             pend.append((out[-1], dict(ev, kind="block", tau=tau, gamma=gamma, block_lists=lists)))
         del Qh, Kh, blist, bcnt, bws, lws, Y, idx
@@ -724,7 +726,8 @@ def varlen_batch(steps, warmup, stream, dev):
     b = make_batch(cfg, VARLEN_LENGTHS)
     cu = [int(v) for v in b["cu_seqlens"]]
     Q, K, V, X = (b[n].to(dev) for n in ("Q", "K", "V", "X"))
-    out = {"workload": f"varlen batch of {len(cu) - 1} ({cfg.name} recipe)", "lengths": VARLEN_LENGTHS,
+    out = {"supplementary": True, "workload": f"varlen batch of {len(cu) - 1} ({cfg.name} recipe)",
+           "lengths": VARLEN_LENGTHS,
            "tokens": cu[-1]}
     for tau in (cfg.tau, 0.5):
         s = binding.shape(cu[-1], cfg.Hq, cfg.Hkv, cfg.d, cfg.q, tau, cfg.dtype)
@@ -889,7 +892,7 @@ def chain_c5(steps, warmup, stream, dev, with_evidence=True):
                                     lambda: binding.dense_attn_causal(st, Q, K, V, X, Yd, dws), max(2, steps // 2), 1,
                                     stream)
                 k, Lp = kLp.tolist()
-                line = {"tau": tau, "k": k, "L_keep": Lp, "pruned_frac": round(k / cfg.L, 4),
+                line = {"supplementary": True, "tau": tau, "k": k, "L_keep": Lp, "pruned_frac": round(k / cfg.L, 4),
                         "layer_ms": round(float(np.median(tl)), 3), "dense_ms": round(float(np.median(td)), 3),
                         "speedup_vs_dense": round(float(np.median(td)) / float(np.median(tl)), 3)}
                 sweep.append(line)
@@ -961,7 +964,8 @@ def graph_replay(steps, warmup, stream, dev):
         eager = timed(lambda: binding.layer(s, Q, K, V, X, Ye, None, ws), steps, warmup, stream)
         g = cap(lambda: binding.layer(s, Q, K, V, X, Yg, None, ws))
         replay = timed(g.replay, steps, warmup, stream)
-        out.append({"workload": cfg.name, "eager_ms": round(eager, 4), "graph_replay_ms": round(replay, 4),
+        out.append({"supplementary": True, "workload": cfg.name, "eager_ms": round(eager, 4),
+                    "graph_replay_ms": round(replay, 4),
                     "bitwise_equal": bool(torch.equal(Ye, Yg))})
         del g, Q, K, V, X, ws, Ye, Yg
     cfg = WORKLOADS[3]
@@ -974,7 +978,8 @@ def graph_replay(steps, warmup, stream, dev):
     eager = timed(lambda: binding.layer_varlen(s, cu, Q, K, V, X, Ye, None, ws), steps, warmup, stream)
     g = cap(lambda: binding.layer_varlen(s, cu, Q, K, V, X, Yg, None, ws))
     replay = timed(g.replay, steps, warmup, stream)
-    out.append({"workload": f"varlen batch of {len(cu) - 1} ({cfg.name} recipe)", "eager_ms": round(eager, 4),
+    out.append({"supplementary": True, "workload": f"varlen batch of {len(cu) - 1} ({cfg.name} recipe)",
+                "eager_ms": round(eager, 4),
                 "graph_replay_ms": round(replay, 4), "bitwise_equal": bool(torch.equal(Ye, Yg))})
     return out
 
