@@ -20,7 +20,9 @@
 // -0.4% at 160K, -1.3% at 192K, -2.0% at 256K, but +1% at 128K, and slower for the dense kernel,
 // whose 8 heads share 2 KV heads).
 //
-// f32 path: a plain vector-ALU kernel (4 lanes per query row, 32-key tiles in LDS), float32 math.
+// f32 path: a vector-ALU kernel (4 lanes per query row, each holding a quarter of the head dimension;
+// 32-key tiles in LDS, the next tile loaded into registers while the current one is used), float32
+// math.
 #include "kern_common.h"
 #include "tsa_internal.h"
 
@@ -484,16 +486,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
 // ------------------------------------------------------------------------------------------------
 template <int D, bool DENSE, bool SPARSE>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
-  constexpr int TPR = 4, BM = 256 / TPR, BN = 32, DPT = D / TPR;
-  __shared__ float smK[BN][D + 1];
-  __shared__ float smV[BN][D + 1];
+  // TPR threads per query row, each owning DPT consecutive head-dim elements (16-byte LDS reads);
+  // 32-key tiles of K and V (rows, padded to a 16-byte multiple) in LDS, the next tile's elements
+  // loaded into registers while the current one is used
+  constexpr int TPR = 4, BM = 256 / TPR, BN = 32, DPT = D / TPR, ROW = D + 4;
+  constexpr int NV4 = BN * D / 4 / 256;     // 16-byte pieces of a K (or V) tile per thread
+  __shared__ __attribute__((aligned(16))) float smK[BN][ROW];
+  __shared__ __attribute__((aligned(16))) float smV[BN][ROW];
   __shared__ uint16_t klist[SPARSE ? kMaxKeyBlocks : 1];
   int h, mb;
   const AttnSeg& sg = block_coords(a, h, mb);
   const int64_t Lp = DENSE ? sg.L : (int64_t)sg.Lp[0];
   const int64_t m0 = (int64_t)mb * BM;
   if (m0 >= Lp) return;
-  const int tid = threadIdx.x, part = tid % TPR;
+  const int tid = threadIdx.x, part = tid % TPR, d0 = part * DPT;
   const int64_t qi = m0 + tid / TPR;
   const int g = h / (a.Hq / a.Hkv);
   const int64_t C = sg.C;
@@ -509,12 +515,18 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const size_t v_base = (size_t)sg.cap_off * (DENSE ? a.Hkv : a.Hq) * D + (size_t)(DENSE ? g : h) * D * C;
 
   float qr[DPT], acc[DPT];
+  {
+    const float4* q4 = reinterpret_cast<const float4*>(Qp + q_row(qi < Lp ? qi : m0) + d0);
 #pragma unroll
-  for (int u = 0; u < DPT; ++u) {
-    qr[u] = qi < Lp ? Qp[q_row(qi) + part + TPR * u] : 0.f;
-    acc[u] = 0.f;
+    for (int u = 0; u < DPT / 4; ++u) {
+      const float4 v = qi < Lp ? q4[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+      qr[4 * u] = v.x; qr[4 * u + 1] = v.y; qr[4 * u + 2] = v.z; qr[4 * u + 3] = v.w;
+    }
   }
+#pragma unroll
+  for (int u = 0; u < DPT; ++u) acc[u] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale * kLog2e;     // scores kept in log2 units
   const int64_t kend = (m0 + BM < Lp ? m0 + BM : Lp);
   // key ranges walked: [0, kend), or (block sparse) every listed key block of this rows' query block
   int nrange = 1;
@@ -524,33 +536,81 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     for (int i = threadIdx.x; i < nrange; i += 256) klist[i] = a.blist[row * a.nbmax + i];
     __syncthreads();
   }
-  for (int rg = 0; rg < nrange; ++rg) {
-  const int64_t kbeg = SPARSE ? (int64_t)klist[rg] * kBlock : 0;
-  const int64_t kstop = SPARSE ? (kbeg + kBlock < kend ? kbeg + kBlock : kend) : kend;
-  for (int64_t key0 = kbeg; key0 < kstop; key0 += BN) {
-    __syncthreads();
-    for (int e = tid; e < BN * D; e += 256) {
-      const int r = e / D, c = e % D;
-      const int64_t j = key0 + r;
-      smK[r][c] = j < Lp ? Kp[k_row(j) + c] : 0.f;
-      const int cv = e / BN, rv = e % BN;           // V^T is token-fastest: coalesce along keys
-      smV[rv][cv] = key0 + rv < Lp ? Vp[v_base + (size_t)cv * C + key0 + rv] : 0.f;
+  auto range_begin = [&](int rg) -> int64_t { return SPARSE ? (int64_t)klist[rg] * kBlock : 0; };
+  auto range_end = [&](int rg) -> int64_t {
+    const int64_t b = range_begin(rg);
+    return SPARSE ? (b + kBlock < kend ? b + kBlock : kend) : kend;
+  };
+  // this thread's pieces of the tile at key0: K piece e -> key row e / (D/4), columns 4 (e % (D/4));
+  // V^T piece e -> head-dim row e / (BN/4), keys 4 (e % (BN/4)).  Keys at or past L' read as zeros.
+  float4 kv[NV4], vv[NV4];
+  auto load_tile = [&](int64_t key0) {
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      kv[i] = key0 + r < Lp ? *reinterpret_cast<const float4*>(Kp + k_row(key0 + r) + 4 * c4)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int cv = e / (BN / 4), k4 = e % (BN / 4);
+      const int64_t j = key0 + 4 * k4;   // V^T rows have capacity C >= key0 + BN: the load stays inside
+      float4 v = *reinterpret_cast<const float4*>(Vp + v_base + (size_t)cv * C + j);
+      if (j + 3 >= Lp) {
+        v.x = j < Lp ? v.x : 0.f;
+        v.y = j + 1 < Lp ? v.y : 0.f;
+        v.z = j + 2 < Lp ? v.z : 0.f;
+        v.w = j + 3 < Lp ? v.w : 0.f;
+      }
+      vv[i] = v;
     }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      *reinterpret_cast<float4*>(&smK[r][4 * c4]) = kv[i];
+      const int cv = e / (BN / 4), k4 = e % (BN / 4);
+      smV[4 * k4][cv] = vv[i].x;
+      smV[4 * k4 + 1][cv] = vv[i].y;
+      smV[4 * k4 + 2][cv] = vv[i].z;
+      smV[4 * k4 + 3][cv] = vv[i].w;
+    }
+  };
+  int rg = 0;
+  int64_t key0 = range_begin(0);
+  load_tile(key0);
+  while (true) {
+    __syncthreads();                    // every thread is done with the previous tile
+    store_tile();
     __syncthreads();
+    // the next tile of the walk, loaded while this one is used
+    int rn = rg;
+    int64_t kn = key0 + BN;
+    if (kn >= range_end(rg)) {
+      rn = rg + 1;
+      kn = rn < nrange ? range_begin(rn) : -1;
+    }
+    if (kn >= 0) load_tile(kn);
     float sc[BN];
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
       float pdot = 0.f;
 #pragma unroll
-      for (int u = 0; u < DPT; ++u) pdot = fmaf(qr[u], smK[j][part + TPR * u], pdot);
+      for (int u = 0; u < DPT / 4; ++u) {
+        const float4 k4 = *reinterpret_cast<const float4*>(&smK[j][d0 + 4 * u]);
+        pdot = fmaf(qr[4 * u], k4.x, pdot);
+        pdot = fmaf(qr[4 * u + 1], k4.y, pdot);
+        pdot = fmaf(qr[4 * u + 2], k4.z, pdot);
+        pdot = fmaf(qr[4 * u + 3], k4.w, pdot);
+      }
       pdot += __shfl_xor(pdot, 1, kWave);
       pdot += __shfl_xor(pdot, 2, kWave);
-      sc[j] = key0 + j <= qi ? pdot * a.scale : -INFINITY;
+      sc[j] = key0 + j <= qi ? pdot * sl2 : -INFINITY;
       mx = fmaxf(mx, sc[j]);
     }
     if (mx > m_run) {
-      const float alpha = expf(m_run - mx);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - mx);
 #pragma unroll
       for (int u = 0; u < DPT; ++u) acc[u] *= alpha;
       l_run *= alpha;
@@ -558,26 +618,35 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
-      const float p = expf(sc[j] - m_run);
+      const float p = __builtin_amdgcn_exp2f(sc[j] - m_run);
       l_run += p;
 #pragma unroll
-      for (int u = 0; u < DPT; ++u) acc[u] = fmaf(p, smV[j][part + TPR * u], acc[u]);
+      for (int u = 0; u < DPT / 4; ++u) {
+        const float4 v4 = *reinterpret_cast<const float4*>(&smV[j][d0 + 4 * u]);
+        acc[4 * u] = fmaf(p, v4.x, acc[4 * u]);
+        acc[4 * u + 1] = fmaf(p, v4.y, acc[4 * u + 1]);
+        acc[4 * u + 2] = fmaf(p, v4.z, acc[4 * u + 2]);
+        acc[4 * u + 3] = fmaf(p, v4.w, acc[4 * u + 3]);
+      }
     }
-  }
+    if (kn < 0) break;
+    rg = rn;
+    key0 = kn;
   }
   if (qi >= Lp) return;
   const float inv_l = 1.f / l_run;
   float* Op = static_cast<float*>(a.O);
   const float* Xp = static_cast<const float*>(a.X);
-  const size_t orow = q_row(qi);
-  float xr[DPT];                        // residual loads before any store (Y may alias X)
+  const size_t orow = q_row(qi) + d0;
+  float4 xr[DPT / 4];                   // residual loads before any store (Y may alias X)
 #pragma unroll
-  for (int u = 0; u < DPT; ++u) xr[u] = DENSE && Xp ? Xp[orow + part + TPR * u] : 0.f;
+  for (int u = 0; u < DPT / 4; ++u)
+    xr[u] = DENSE && Xp ? *reinterpret_cast<const float4*>(Xp + orow + 4 * u) : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int u = 0; u < DPT; ++u) {
-    float v = acc[u] * inv_l;
-    if (DENSE && Xp) v += xr[u];
-    Op[orow + part + TPR * u] = v;
+  for (int u = 0; u < DPT / 4; ++u) {
+    float4 v = make_float4(acc[4 * u] * inv_l, acc[4 * u + 1] * inv_l, acc[4 * u + 2] * inv_l, acc[4 * u + 3] * inv_l);
+    if (DENSE && Xp) { v.x += xr[u].x; v.y += xr[u].y; v.z += xr[u].z; v.w += xr[u].w; }
+    *reinterpret_cast<float4*>(Op + orow + 4 * u) = v;
   }
 }
 
