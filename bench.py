@@ -479,8 +479,9 @@ def measured_traffic(cfg):
         return None
 
 
-STAGE_SOURCES = {"score": "score.hip", "budget": "select.hip", "select": "select.hip", "gather": "move.hip",
-                 "scatter": "move.hip"}
+# the sources of each stage's kernels (the score stage includes the layer score's kernels)
+STAGE_SOURCES = {"score": ("score.hip", "select.hip"), "budget": ("select.hip",), "select": ("select.hip",),
+                 "gather": ("move.hip",), "scatter": ("move.hip",)}
 STAGE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stages_L131072_bf16.txt")
 
 
@@ -568,9 +569,10 @@ def measured_stage_traffic(cfg):
     if (kv.get("workload_L"), kv.get("workload_Hq"), kv.get("workload_d")) != (str(cfg.L), str(cfg.Hq), str(cfg.d)):
         return {}
     out = {}
-    for st, src in STAGE_SOURCES.items():
-        h = source_hash(os.path.join(ROOT, "token_sparse_attention_amd", "csrc", src))
-        if kv.get(f"source_sha256_16 {src}") == h and f"{st}_hbm_bytes" in kv:
+    for st, srcs in STAGE_SOURCES.items():
+        same = all(kv.get(f"source_sha256_16 {src}") == source_hash(os.path.join(ROOT, "token_sparse_attention_amd",
+                                                                                "csrc", src)) for src in srcs)
+        if same and f"{st}_hbm_bytes" in kv:
             out[st] = int(float(kv[f"{st}_hbm_bytes"]))
     return out
 

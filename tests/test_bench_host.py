@@ -102,9 +102,9 @@ def test_stage_traffic_only_for_unchanged_sources(monkeypatch):
     got = bench.measured_stage_traffic(prof)
     kv = dict(ln.split(":", 1) for ln in open(bench.STAGE_TRAFFIC_FILE) if ":" in ln and not ln.startswith("#"))
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    for st, src in bench.STAGE_SOURCES.items():
-        now = bench.source_hash(os.path.join(ROOT, "token_sparse_attention_amd", "csrc", src))
-        if kv[f"source_sha256_16 {src}"] == now:
+    for st, srcs in bench.STAGE_SOURCES.items():
+        now = [bench.source_hash(os.path.join(ROOT, "token_sparse_attention_amd", "csrc", src)) for src in srcs]
+        if all(kv[f"source_sha256_16 {src}"] == h for src, h in zip(srcs, now)):
             assert got[st] == int(kv[f"{st}_hbm_bytes"])
         else:
             assert st not in got

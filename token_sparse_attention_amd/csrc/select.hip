@@ -28,8 +28,9 @@ int64_t layer_tiles(int64_t L) { return (L + kLayerTile - 1) / kLayerTile + 1; }
 int64_t select_tiles(int64_t L) { return (L + kSelTile - 1) / kSelTile; }
 
 // ---- layer score --------------------------------------------------------------------------------
-// S[t] = sum over heads in head order (float64); s_l = S / total with the total summed once, in a
-// fixed order, by a single block.  One token per thread, so a launch has L/256 blocks.
+// S[t] = sum over heads in head order (float64); s_l = S / total, the total summed in one fixed
+// order (every block of the normalisation forms the same value).  One token per thread, so a launch
+// has L/256 blocks.
 
 __global__ __launch_bounds__(256) void layer_sum_kernel(const float* __restrict__ s_h, int64_t L, int Hq,
                                                         double* __restrict__ S, double* __restrict__ tile_sum) {
@@ -68,25 +69,23 @@ __device__ double tile_total(const double* __restrict__ tile_sum, int64_t ntiles
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
-__global__ __launch_bounds__(256) void layer_total_kernel(double* __restrict__ tile_sum, int64_t ntiles) {
-  __shared__ double red[4];
-  const double total = tile_total(tile_sum, ntiles, red);
-  if (threadIdx.x == 0) tile_sum[ntiles] = total;
-}
-
+// s_l = S / total; each block sums the tile sums itself (ntiles = L / 256 of them, a few KB read
+// from L2), so the total needs no launch of its own
 __global__ __launch_bounds__(256) void layer_norm_kernel(const double* __restrict__ S,
-                                                         const double* __restrict__ total, int64_t L,
-                                                         float* __restrict__ s_l) {
+                                                         const double* __restrict__ tile_sum, int64_t ntiles,
+                                                         int64_t L, float* __restrict__ s_l) {
+  __shared__ double red[4];
   const int64_t t = (int64_t)blockIdx.x * kLayerTile + threadIdx.x;
-  if (t < L) s_l[t] = (float)(S[t] / total[0]);
+  const double s = t < L ? S[t] : 0.0;        // loaded before the total's barrier
+  const double total = tile_total(tile_sum, ntiles, red);
+  if (t < L) s_l[t] = (float)(s / total);
 }
 
 hipError_t launch_layer_score(const float* s_h, int64_t L, int Hq, double* S, double* tile_sum,
                               float* s_l, hipStream_t st) {
   const unsigned n = (unsigned)(layer_tiles(L) - 1);
   layer_sum_kernel<<<n, 256, 0, st>>>(s_h, L, Hq, S, tile_sum);
-  layer_total_kernel<<<1, 256, 0, st>>>(tile_sum, n);
-  layer_norm_kernel<<<n, 256, 0, st>>>(S, tile_sum + n, L, s_l);
+  layer_norm_kernel<<<n, 256, 0, st>>>(S, tile_sum, n, L, s_l);
   return hipGetLastError();
 }
 
