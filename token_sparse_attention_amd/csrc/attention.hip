@@ -20,9 +20,9 @@
 // -0.4% at 160K, -1.3% at 192K, -2.0% at 256K, but +1% at 128K, and slower for the dense kernel,
 // whose 8 heads share 2 KV heads).
 //
-// f32 path: a vector-ALU kernel (4 lanes per query row, each holding a quarter of the head dimension;
-// 32-key tiles in LDS, the next tile loaded into registers while the current one is used), float32
-// math.
+// f32 path: a vector-ALU kernel (4 lanes per query row, each holding a quarter of the head dimension,
+// 64 rows per block, or 16 lanes and 16 rows when the launch is small; 32-key tiles in LDS, the next
+// tile loaded into registers while the current one is used), float32 math.
 #include "kern_common.h"
 #include "tsa_internal.h"
 
@@ -43,6 +43,18 @@ constexpr float kLazyLog2 = 8.0f;
 // (two per CU) fill the chip better there than the shared tiles save (measured layer times, 32/8
 // heads: 4K -10%, 32K -1%, 48K -0.8%, but 64K +0.3%, 96K +2.5%, 128K +1.5%).
 constexpr int kAttnWaves = 8;
+// Lanes per query row of the f32 kernel (its 256-thread blocks hold 256 / lanes rows).  A launch
+// that would have fewer than kF32SplitBelow blocks of 64 rows leaves CUs idle and is bound by the
+// longest block's walk over its key tiles: it splits each row 16 ways over 16-row blocks instead
+// (measured: tiny fp32 layer, L = 1024 and 4 heads, dense 0.228 -> 0.138 ms; L = 2500 and 8 heads
+// 1.01 -> 0.79 ms; but at L = 4096 and 8 heads, 512 such blocks, 0.91 -> 1.11 ms, since the 16
+// lanes of a row repeat its exponentials and shuffles).  Both give the same bits: the dot product
+// is summed in the same order, and a row's keys are walked in the same tiles (the extra tiles a
+// 64-row block walks are fully masked for the row, adding exact zeros).
+constexpr int kF32Lanes = 4, kF32SplitLanes = 16;
+constexpr int64_t kF32SplitBelow = 512;
+
+static int f32_lanes(int64_t blocks64) { return blocks64 < kF32SplitBelow ? kF32SplitLanes : kF32Lanes; }
 constexpr int64_t kShortMaxLen = 49152;
 
 // One sequence of a launch.  A launch covers up to kMaxSeg sequences packed along the token
@@ -484,12 +496,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_bf16_kernel(AttnArgs a) 
 // ------------------------------------------------------------------------------------------------
 // f32, vector ALU
 // ------------------------------------------------------------------------------------------------
-template <int D, bool DENSE, bool SPARSE>
+template <int D, bool DENSE, bool SPARSE, int TPR>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   // TPR threads per query row, each owning DPT consecutive head-dim elements (16-byte LDS reads);
   // 32-key tiles of K and V (rows, padded to a 16-byte multiple) in LDS, the next tile's elements
   // loaded into registers while the current one is used
-  constexpr int TPR = 4, BM = 256 / TPR, BN = 32, DPT = D / TPR, ROW = D + 4;
+  constexpr int BM = 256 / TPR, BN = 32, DPT = D / TPR, ROW = D + 4;
+  constexpr int CH = D / kF32SplitLanes, NCH = DPT / CH;   // dot-product partials: length, per lane
   constexpr int NV4 = BN * D / 4 / 256;     // 16-byte pieces of a K (or V) tile per thread
   __shared__ __attribute__((aligned(16))) float smK[BN][ROW];
   __shared__ __attribute__((aligned(16))) float smV[BN][ROW];
@@ -595,17 +608,29 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < BN; ++j) {
-      float pdot = 0.f;
+      // the dot product in one fixed order for either lane count: D / 16 consecutive products per
+      // partial sum, then a pairwise tree over the 16 partials (inside the lane, then across lanes)
+      float part[NCH];
 #pragma unroll
-      for (int u = 0; u < DPT / 4; ++u) {
-        const float4 k4 = *reinterpret_cast<const float4*>(&smK[j][d0 + 4 * u]);
-        pdot = fmaf(qr[4 * u], k4.x, pdot);
-        pdot = fmaf(qr[4 * u + 1], k4.y, pdot);
-        pdot = fmaf(qr[4 * u + 2], k4.z, pdot);
-        pdot = fmaf(qr[4 * u + 3], k4.w, pdot);
+      for (int c = 0; c < NCH; ++c) {
+        part[c] = 0.f;
+#pragma unroll
+        for (int u = 0; u < CH / 4; ++u) {
+          const int e = c * CH + 4 * u;
+          const float4 k4 = *reinterpret_cast<const float4*>(&smK[j][d0 + e]);
+          part[c] = fmaf(qr[e], k4.x, part[c]);
+          part[c] = fmaf(qr[e + 1], k4.y, part[c]);
+          part[c] = fmaf(qr[e + 2], k4.z, part[c]);
+          part[c] = fmaf(qr[e + 3], k4.w, part[c]);
+        }
       }
-      pdot += __shfl_xor(pdot, 1, kWave);
-      pdot += __shfl_xor(pdot, 2, kWave);
+#pragma unroll
+      for (int w = 1; w < NCH; w <<= 1)
+#pragma unroll
+        for (int c = 0; c < NCH; c += 2 * w) part[c] += part[c + w];
+      float pdot = part[0];
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) pdot += __shfl_xor(pdot, o, kWave);
       sc[j] = key0 + j <= qi ? pdot * sl2 : -INFINITY;
       mx = fmaxf(mx, sc[j]);
     }
@@ -652,7 +677,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 template <int D, bool DENSE, bool SPARSE = false, bool FUSED = false>
 static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_t st, int nw = kAttnWaves,
-                           bool wide = false) {
+                           bool wide = false, int f32lanes = kF32Lanes) {
   if (dtype == 1) {
     if constexpr (SPARSE) {
       attn_bf16_kernel<D, DENSE, SPARSE, FUSED, 4><<<(unsigned)nblocks, 256, 0, st>>>(a);
@@ -669,8 +694,10 @@ static hipError_t run_attn(int dtype, const AttnArgs& a, int nblocks, hipStream_
       if (nw == 4) attn_bf16_kernel<D, DENSE, SPARSE, FUSED, 4><<<(unsigned)nblocks, 256, 0, st>>>(a);
       else attn_bf16_kernel<D, DENSE, SPARSE, FUSED, kAttnWaves><<<(unsigned)nblocks, 64 * kAttnWaves, 0, st>>>(a);
     }
-  } else if (!FUSED)
-    attn_f32_kernel<D, DENSE, SPARSE><<<(unsigned)nblocks, 256, 0, st>>>(a);
+  } else if (!FUSED) {
+    if (f32lanes == kF32SplitLanes) attn_f32_kernel<D, DENSE, SPARSE, kF32SplitLanes><<<(unsigned)nblocks, 256, 0, st>>>(a);
+    else attn_f32_kernel<D, DENSE, SPARSE, kF32Lanes><<<(unsigned)nblocks, 256, 0, st>>>(a);
+  }
   else
     return hipErrorInvalidValue;         // the fused layer is bf16 only
   return hipGetLastError();
@@ -689,7 +716,10 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
     const int nw = longest <= kShortMaxLen ? 4 : kAttnWaves;
     // a sequence's K rows span L * Hkv * d * 2 bytes from its first token
     const bool wide = (uint64_t)longest * (uint64_t)Hkv * (uint64_t)d * 2u >= (uint64_t(1) << 32);
-    const int bm = dtype == 1 ? 32 * nw : 64;      // query rows per block
+    int64_t blocks64 = 0;                          // f32: blocks of 64 rows over the launch
+    for (int i = 0; i < a.nseg; ++i) blocks64 += (seqs[first + i].L + 63) / 64 * Hq;
+    const int lanes = f32_lanes(blocks64);
+    const int bm = dtype == 1 ? 32 * nw : 256 / lanes;      // query rows per block
     int nblocks = 0;
     for (int i = 0; i < a.nseg; ++i) {
       const AttnSeqDesc& q = seqs[first + i];
@@ -705,9 +735,11 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
       e = d == 128 ? run_attn<128, false, false, true>(dtype, a, nblocks, st, nw, wide)
                    : run_attn<64, false, false, true>(dtype, a, nblocks, st, nw, wide);
     else if (d == 128)
-      e = dense ? run_attn<128, true>(dtype, a, nblocks, st, nw) : run_attn<128, false>(dtype, a, nblocks, st, nw);
+      e = dense ? run_attn<128, true>(dtype, a, nblocks, st, nw, false, lanes)
+                : run_attn<128, false>(dtype, a, nblocks, st, nw, false, lanes);
     else
-      e = dense ? run_attn<64, true>(dtype, a, nblocks, st, nw) : run_attn<64, false>(dtype, a, nblocks, st, nw);
+      e = dense ? run_attn<64, true>(dtype, a, nblocks, st, nw, false, lanes)
+                : run_attn<64, false>(dtype, a, nblocks, st, nw, false, lanes);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -716,7 +748,8 @@ hipError_t launch_attention_varlen(int dtype, int d, bool dense, const void* Q, 
 hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const void* Kh, const void* Vht,
                                          const int32_t* Lp_dev, int64_t L, int Hq, int Hkv, int64_t C,
                                          const uint16_t* list, const int32_t* count, void* Oh, hipStream_t st) {
-  const int bm = dtype == 1 ? 128 : 64;
+  const int lanes = f32_lanes((L + 63) / 64 * Hq);
+  const int bm = dtype == 1 ? 128 : 256 / lanes;
   AttnArgs a{};
   a.Q = Qh; a.K = Kh; a.Vt = Vht; a.X = nullptr; a.O = Oh;
   a.Hq = Hq; a.Hkv = Hkv; a.scale = (float)(1.0 / sqrt((double)d));
@@ -724,7 +757,8 @@ hipError_t launch_attention_block_sparse(int dtype, int d, const void* Qh, const
   a.nseg = 1;
   a.seg[0] = AttnSeg{0, 0, L, C, Lp_dev, nullptr, 0, (int)((L + bm - 1) / bm), 8};
   const int nblocks = a.seg[0].nmb * Hq;
-  return d == 128 ? run_attn<128, false, true>(dtype, a, nblocks, st) : run_attn<64, false, true>(dtype, a, nblocks, st);
+  return d == 128 ? run_attn<128, false, true>(dtype, a, nblocks, st, kAttnWaves, false, lanes)
+                  : run_attn<64, false, true>(dtype, a, nblocks, st, kAttnWaves, false, lanes);
 }
 
 hipError_t launch_attention(int dtype, int d, bool dense, const void* Q, const void* K,
