@@ -17,7 +17,7 @@
 namespace tsa {
 
 constexpr int kScoreKeys = 256;   // keys per block = threads per block
-constexpr int kQChunk = 32;       // recent-query rows staged in LDS at a time
+constexpr int kQChunk = 32;       // recent-query rows staged in LDS at a time (16 when a group has no more)
 
 int64_t score_blocks(int64_t L) { return (L + kScoreKeys - 1) / kScoreKeys; }
 
@@ -62,13 +62,14 @@ __device__ __forceinline__ void load_row(const T* __restrict__ p, float (&r)[D])
 }
 
 // Rows of group g are ordered head-major: row r -> query head g*G + r/q, position L - q + r%q.
-template <typename T, int D, int PASS>
+// QC rows are formed at a time; every row's arithmetic is the same for either QC.
+template <typename T, int D, int PASS, int QC>
 __global__ __launch_bounds__(kScoreKeys) void score_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, int64_t L, int Hq, int Hkv, int q,
     double scale, double2* __restrict__ part, const double2* __restrict__ rowstat,
     float* __restrict__ s_h) {
-  __shared__ __attribute__((aligned(16))) float qs[kQChunk][D];
-  __shared__ double zs[kQChunk][kScoreKeys];
+  __shared__ __attribute__((aligned(16))) float qs[QC][D];
+  __shared__ double zs[QC][kScoreKeys];
   const int g = blockIdx.y;
   const int64_t blk = blockIdx.x, nblk = gridDim.x;
   const int tid = threadIdx.x;
@@ -85,9 +86,9 @@ __global__ __launch_bounds__(kScoreKeys) void score_kernel(
   }
 
   double hsum = 0.0;
-  for (int r0 = 0; r0 < R; r0 += kQChunk) {
+  for (int r0 = 0; r0 < R; r0 += QC) {
     __syncthreads();
-    for (int e = tid; e < kQChunk * D; e += kScoreKeys) {
+    for (int e = tid; e < QC * D; e += kScoreKeys) {
       const int rr = e / D, c = e % D, r = r0 + rr;
       float v = 0.f;
       if (r < R) {
@@ -99,14 +100,14 @@ __global__ __launch_bounds__(kScoreKeys) void score_kernel(
     }
     __syncthreads();
     // acc[j] = <Q row r0+j, K row t>; each K element is widened once and used for all 32 rows.
-    double acc[kQChunk];
+    double acc[QC];
 #pragma unroll
-    for (int j = 0; j < kQChunk; ++j) acc[j] = 0.0;
+    for (int j = 0; j < QC; ++j) acc[j] = 0.0;
 #pragma unroll
     for (int c4 = 0; c4 < D / 4; ++c4) {
       const double k0 = kr[4 * c4], k1 = kr[4 * c4 + 1], k2 = kr[4 * c4 + 2], k3 = kr[4 * c4 + 3];
 #pragma unroll
-      for (int j = 0; j < kQChunk; ++j) {
+      for (int j = 0; j < QC; ++j) {
         const float4 qv = *reinterpret_cast<const float4*>(&qs[j][4 * c4]);
         acc[j] = fma((double)qv.x, k0, acc[j]);
         acc[j] = fma((double)qv.y, k1, acc[j]);
@@ -115,10 +116,10 @@ __global__ __launch_bounds__(kScoreKeys) void score_kernel(
       }
     }
 #pragma unroll
-    for (int j = 0; j < kQChunk; ++j) zs[j][tid] = acc[j];
+    for (int j = 0; j < QC; ++j) zs[j][tid] = acc[j];
     // (each thread reads back only its own column: no barrier needed)
 #pragma unroll 1
-    for (int j = 0; j < kQChunk; ++j) {
+    for (int j = 0; j < QC; ++j) {
       const int r = r0 + j;
       if (r >= R) break;
       const int i = r % q;
@@ -170,11 +171,14 @@ static hipError_t run_score(const void* Q, const void* K, int64_t L, int Hq, int
   const dim3 grid((unsigned)score_blocks(L), (unsigned)Hkv);
   const T* Qt = static_cast<const T*>(Q);
   const T* Kt = static_cast<const T*>(K);
-  score_kernel<T, D, 1><<<grid, kScoreKeys, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, scale, part, rowstat, s_h);
+  const bool small = (Hq / Hkv) * q <= kQChunk / 2;   // a group's rows fit one 16-row chunk
+  if (small) score_kernel<T, D, 1, kQChunk / 2><<<grid, kScoreKeys, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, scale, part, rowstat, s_h);
+  else score_kernel<T, D, 1, kQChunk><<<grid, kScoreKeys, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, scale, part, rowstat, s_h);
   const int64_t nrows = (int64_t)Hq * q;     // Hkv groups x (Hq/Hkv) * q rows
   const int64_t nparts = score_blocks(L) * (kScoreKeys / kWave);
   score_combine_kernel<<<(unsigned)((nrows + 3) / 4), 256, 0, st>>>(part, nrows, nparts, 1.0, rowstat);
-  score_kernel<T, D, 2><<<grid, kScoreKeys, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, scale, part, rowstat, s_h);
+  if (small) score_kernel<T, D, 2, kQChunk / 2><<<grid, kScoreKeys, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, scale, part, rowstat, s_h);
+  else score_kernel<T, D, 2, kQChunk><<<grid, kScoreKeys, 0, st>>>(Qt, Kt, L, Hq, Hkv, q, scale, part, rowstat, s_h);
   return hipGetLastError();
 }
 
